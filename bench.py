@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Benchmark: one M = 8 speculative-decoding verify pass over the full weight
+stream of the 27B hybrid (64 layers: 48 Gated DeltaNet + 16 full attention,
+SwiGLU MLP, vocabulary head with argmax + greedy accept), 17,555,292,160
+bytes of NVFP4 + FP8 weights, on one MI355X.
+
+A step is one pass: 257 libverify launches in model order, captured once into
+a HIP graph and replayed. Weights are seeded synthetic tensors already resident
+in HBM. Printed: one JSON line (see the keys below).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HIDDEN, INTER, VOCAB, LAYERS = 5120, 17408, 248320, 64
+GDN_IN, MIX_OUT_K = 16384, 6144
+ATTN_QGKV = 12288 + 1024 + 1024
+M_ROWS = 8
+ALPHA = 4.80                      # accepted tokens per verify pass used for tok/s
+HBM_PEAK_GBPS = 8000.0            # MI355X published HBM3E bandwidth
+
+METRIC = "ms per M=8 verify pass (17.6 GB weights), effective HBM GB/s and % of peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def nvfp4_bytes(n, k):
+    return n * k // 16 * 9
+
+
+def schedule():
+    """(kind, fmt, N_out, K) in model order; layer l is full attention iff l % 4 == 3."""
+    out = []
+    for layer in range(LAYERS):
+        if layer % 4 == 3:
+            out.append(("attn_qgkv", "fp8", ATTN_QGKV, HIDDEN))
+            out.append(("attn_o", "fp8", HIDDEN, MIX_OUT_K))
+        else:
+            out.append(("gdn_in", "fp8", GDN_IN, HIDDEN))
+            out.append(("gdn_out", "fp8", HIDDEN, MIX_OUT_K))
+        out.append(("mlp_gate_up", "nvfp4_silu", INTER, HIDDEN))
+        out.append(("mlp_down", "nvfp4", HIDDEN, INTER))
+    out.append(("lm_head", "head", VOCAB, HIDDEN))
+    return out
+
+
+def weight_bytes(fmt, n, k):
+    if fmt == "fp8":
+        return n * k
+    if fmt == "nvfp4_silu":
+        return nvfp4_bytes(2 * n, k)
+    return nvfp4_bytes(n, k)
+
+
+def act_bytes(n, k, m=M_ROWS):
+    return m * k * 2 + m * n * 2
+
+
+class Pass:
+    """Device buffers and the launch list of one verify pass."""
+
+    def __init__(self, torch, ops, inputs, dev):
+        self.torch, self.ops, self.dev = torch, ops, dev
+        self.items = schedule()
+        t0 = time.time()
+        self.w = []
+        for i, (kind, fmt, n, k) in enumerate(self.items):
+            key = (5, i)
+            if fmt == "fp8":
+                self.w.append((inputs.device_fp8_weights(key, n, k, dev),))
+            elif fmt == "nvfp4_silu":
+                self.w.append(inputs.device_nvfp4_weights(key, 2 * n, k, dev))
+            else:
+                self.w.append(inputs.device_nvfp4_weights(key, n, k, dev))
+        torch.cuda.synchronize()
+        log(f"weights generated on device in {time.time() - t0:.1f}s")
+        bf = torch.bfloat16
+        self.x_hidden = inputs.device_x_bf16((5, 1000), M_ROWS, HIDDEN, dev)
+        self.x_mix = inputs.device_x_bf16((5, 1001), M_ROWS, MIX_OUT_K, dev)
+        self.h_final = inputs.device_x_bf16((5, 1002), M_ROWS, HIDDEN, dev)
+        self.y_in = torch.empty((M_ROWS, max(GDN_IN, ATTN_QGKV)), dtype=bf, device=dev)
+        self.y_hid = torch.empty((M_ROWS, HIDDEN), dtype=bf, device=dev)
+        self.h_mlp = torch.empty((M_ROWS, INTER), dtype=bf, device=dev)
+        self.argmax = torch.empty((M_ROWS,), dtype=torch.int32, device=dev)
+        self.maxlogit = torch.empty((M_ROWS,), dtype=torch.float32, device=dev)
+        self.accept = torch.empty((1,), dtype=torch.int32, device=dev)
+        self.commit = torch.empty((1, M_ROWS), dtype=torch.int32, device=dev)
+        self.drafts = torch.zeros((1, M_ROWS - 1), dtype=torch.int32, device=dev)
+        self.ws = {}
+        for kind, fmt, n, k in self.items:
+            op = {"fp8": ops.VQ_OP_FP8, "nvfp4": ops.VQ_OP_NVFP4, "nvfp4_silu": ops.VQ_OP_NVFP4_SILU_MUL,
+                  "head": ops.VQ_OP_LMHEAD}[fmt]
+            if (op, n, k) not in self.ws:
+                self.ws[(op, n, k)] = ops.workspace(op, M_ROWS, n, k, dev)
+        self.weight_bytes = sum(weight_bytes(f, n, k) for _, f, n, k in self.items)
+        self.act_bytes = sum(act_bytes(n, k) for _, _, n, k in self.items)
+
+    def launch(self, i):
+        ops = self.ops
+        kind, fmt, n, k = self.items[i]
+        w = self.w[i]
+        if fmt == "fp8":
+            x = self.x_hidden if k == HIDDEN else self.x_mix
+            y = self.y_in[:, :n] if n != HIDDEN else self.y_hid
+            if n != HIDDEN:
+                y = self.y_in.view(-1)[: M_ROWS * n].view(M_ROWS, n)
+            ops.vq_gemm_fp8(x, w[0], 1.0, y, workspace=self.ws[(ops.VQ_OP_FP8, n, k)])
+        elif fmt == "nvfp4_silu":
+            ops.vq_gemm_nvfp4(self.x_hidden, w[0], w[1], 1.0, self.h_mlp, epilogue=ops.VQ_EPI_SILU_MUL,
+                              workspace=self.ws[(ops.VQ_OP_NVFP4_SILU_MUL, n, k)])
+        elif fmt == "nvfp4":
+            ops.vq_gemm_nvfp4(self.h_mlp, w[0], w[1], 1.0, self.y_hid, workspace=self.ws[(ops.VQ_OP_NVFP4, n, k)])
+        else:
+            ops.vq_lmhead_argmax_accept(self.h_final, w[0], w[1], 1.0, self.drafts, 1, M_ROWS, self.argmax,
+                                        self.accept, maxlogit_out=self.maxlogit, commit_out=self.commit,
+                                        workspace=self.ws[(ops.VQ_OP_LMHEAD, n, k)])
+
+    def run(self):
+        for i in range(len(self.items)):
+            self.launch(i)
+
+
+def measure_probes(torch, ops, dev, gib=4, reps=10):
+    nbytes = gib << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    out = {}
+    for name, fn, moved in (("copy", lambda: ops.vq_probe_copy(src, dst), 2 * nbytes),
+                            ("read", lambda: ops.vq_probe_read(src, sink), nbytes)):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def per_kind_durations(torch, p, reps=2):
+    """Eager pass with an event pair around every launch (same stream)."""
+    evs = []
+    for _ in range(reps):
+        for i in range(len(p.items)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            p.launch(i)
+            b.record()
+            evs.append((i, a, b))
+    torch.cuda.synchronize()
+    acc = {}
+    for i, a, b in evs:
+        kind, fmt, n, k = p.items[i]
+        d = acc.setdefault(kind, {"ms": 0.0, "count": 0, "wbytes": weight_bytes(fmt, n, k), "abytes": act_bytes(n, k)})
+        d["ms"] += a.elapsed_time(b)
+        d["count"] += 1
+    res = {}
+    for kind, d in acc.items():
+        us = d["ms"] / d["count"] * 1e3
+        res[kind] = {"avg_us": round(us, 2), "launches_per_pass": d["count"] // reps,
+                     "weight_bytes": d["wbytes"], "gbps": round(d["wbytes"] / (us * 1e-6) / 1e9, 1)}
+    return res
+
+
+def dominant_kernel_duration(torch, p, reps=3):
+    """Average duration of the [gate; up] + SiLU*up launch (the kernel with the
+    largest share of pass time), timed with events on its own stream over
+    reps x 64 chained launches rotating over the 64 layers' weights."""
+    idx = [i for i, it in enumerate(p.items) if it[0] == "mlp_gate_up"]
+    for i in idx[:4]:
+        p.launch(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for i in idx:
+            p.launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(idx)) * 1e-3   # seconds
+
+
+def cpu_baseline(inputs_mod, budget_s=20.0):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    4096-row slices of an NVFP4 gate/up matrix and of an FP8 GDN in-projection
+    at M = 8, repeated until the time budget is spent; scaled to the pass's
+    bytes of each format."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    rows = 4096
+    x = inputs_mod.x_bf16((6, 0), M_ROWS, HIDDEN)
+    codes, scales = inputs_mod.nvfp4_weights((6, 1), rows, HIDDEN)
+    w8 = inputs_mod.fp8_weights((6, 2), rows, HIDDEN)
+    t_f4 = t_f8 = 0.0
+    n_f4 = n_f8 = 0
+    t_start = time.time()
+    while time.time() - t_start < budget_s or n_f4 == 0 or n_f8 == 0:
+        t0 = time.perf_counter()
+        O.gemm_nvfp4(x, codes, scales, 1.0)
+        t_f4 += time.perf_counter() - t0
+        n_f4 += 1
+        t0 = time.perf_counter()
+        O.gemm_fp8(x, w8, 1.0)
+        t_f8 += time.perf_counter() - t0
+        n_f8 += 1
+    gbps_f4 = nvfp4_bytes(rows, HIDDEN) * n_f4 / t_f4 / 1e9
+    gbps_f8 = rows * HIDDEN * n_f8 / t_f8 / 1e9
+    items = schedule()
+    b_f4 = sum(weight_bytes(f, n, k) for _, f, n, k in items if f != "fp8")
+    b_f8 = sum(weight_bytes(f, n, k) for _, f, n, k in items if f == "fp8")
+    s_pass = b_f4 / (gbps_f4 * 1e9) + b_f8 / (gbps_f8 * 1e9)
+    return {
+        "value": round((b_f4 + b_f8) / s_pass / 1e9, 4),
+        "unit": "GB/s",
+        "ms_per_pass": round(s_pass * 1e3, 1),
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, M=8: {n_f4}x NVFP4 4096x5120 and {n_f8}x FP8 4096x5120 row slices "
+                   f"({t_f4 + t_f8:.1f}s); NVFP4 {gbps_f4:.3f} GB/s, FP8 {gbps_f8:.3f} GB/s, scaled to the pass's "
+                   f"{b_f4} NVFP4 + {b_f8} FP8 bytes"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the verify-pass weight stream is built and timed on a single "
+              f"MI355X (asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_block_scaled_vq_amd import inputs, ops
+    ops.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    probes = measure_probes(torch, ops, dev)
+    log(f"probes: copy {probes['copy']:.0f} GB/s, read {probes['read']:.0f} GB/s")
+
+    p = Pass(torch, ops, inputs, dev)
+    # a realistic draft block: the target's own argmax with p = 0.7 per draft
+    p.run()
+    torch.cuda.synchronize()
+    p.drafts.copy_(inputs.device_drafts((5, 2000), p.argmax.view(1, M_ROWS), VOCAB))
+
+    # capture the pass once, replay it
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        p.run()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            p.run()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    gbps = p.weight_bytes / dt / 1e9
+    log(f"pass: {dt * 1e3:.3f} ms, {gbps:.0f} GB/s effective")
+
+    # eager (ungraphed) pass for the per-kernel table and the graph benefit
+    t0 = time.perf_counter()
+    p.run()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3
+    kinds = per_kind_durations(torch, p)
+    dom_s = dominant_kernel_duration(torch, p)
+    gu_w = weight_bytes("nvfp4_silu", INTER, HIDDEN)
+    gu_a = act_bytes(INTER, HIDDEN)
+    achieved = (gu_w + gu_a) / dom_s / 1e9
+    accept = int(p.accept.item())
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(inputs, args.cpu_budget)
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded NVFP4/FP8 weights of the 27B hybrid's shapes, generated on the device)",
+        "config": {
+            "workload": "full M=8 verify-pass weight stream: 64 layers (48 GDN FP8 in/out, 16 attention FP8 "
+                        "q+gate+k+v/o), 64 NVFP4 SwiGLU MLPs, NVFP4 vocab head + argmax + accept",
+            "rows": M_ROWS, "launches": len(p.items), "weight_bytes": p.weight_bytes,
+            "activation_bytes": p.act_bytes, "graph": True,
+        },
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+        "pct_of_measured_copy_bw": round(100 * gbps / probes["copy"], 1),
+        "pct_of_measured_read_bw": round(100 * gbps / probes["read"], 1),
+        "measured_copy_gbps": round(probes["copy"], 1),
+        "measured_read_gbps": round(probes["read"], 1),
+        "tok_s_at_alpha_4_80": round(ALPHA / dt, 1),
+        "eager_ms_per_pass": round(eager_ms, 3),
+        "accept_len_last_pass": accept,
+        "kernels": kinds,
+        "roofline": {
+            "kernel": "vq_gemm_kernel<NVFP4, SILU_MUL, M<=8> ([gate;up] 34816x5120 + SiLU*up)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(dom_s * 1e6, 2),
+            "bytes_per_launch": gu_w + gu_a,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,289 @@
+// libverify C ABI: argument validation, the gfx950 gate, the stream-K schedule
+// and workspace layout, and dispatch to the HIP kernels. See include/libverify.h
+// for the contract of every entry point.
+#include "libverify.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "vq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int32_t fail(int32_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int32_t check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(VQ_ERR_DEVICE, "no HIP device is available");
+  }
+  if (dev >= kMaxDevices) return fail(VQ_ERR_DEVICE, "device index %d out of range", dev);
+  int st = g_dev_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(VQ_ERR_DEVICE, "hipGetDeviceProperties failed on device %d", dev);
+    }
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_relaxed);
+    if (st == 2) return fail(VQ_ERR_DEVICE, "device %d is %s, libverify is built for gfx950", dev, prop.gcnArchName);
+  }
+  return st == 1 ? VQ_OK : fail(VQ_ERR_DEVICE, "device %d is not gfx950", dev);
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool shape_ok(int32_t M, int32_t N, int32_t K) {
+  return M >= 1 && M <= vq::kMaxRows && N >= 1 && N <= (1 << 30) && K >= vq::kIterK && K % vq::kIterK == 0 &&
+         K <= (1 << 24);
+}
+
+int32_t check_shape(int32_t M, int32_t N, int32_t K) {
+  if (M < 1 || M > vq::kMaxRows) return fail(VQ_ERR_SHAPE, "M = %d outside [1, %d]", M, vq::kMaxRows);
+  if (N < 1 || N > (1 << 30)) return fail(VQ_ERR_SHAPE, "N = %d outside [1, 2^30]", N);
+  if (K < vq::kIterK || K % vq::kIterK != 0 || K > (1 << 24))
+    return fail(VQ_ERR_SHAPE, "K = %d must be a positive multiple of %d (at most 2^24)", K, vq::kIterK);
+  return VQ_OK;
+}
+
+int32_t check_ws(const vq::Schedule& s, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(VQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", s.bytes);
+  if (!aligned(ws, 16)) return fail(VQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (ws_bytes < s.bytes) return fail(VQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, s.bytes);
+  return VQ_OK;
+}
+
+void bind_workspace(vq::GemmParams& p, const vq::Schedule& s, void* ws) {
+  char* base = static_cast<char*>(ws);
+  p.partials = reinterpret_cast<float*>(base + s.off_partials);
+  p.counters = reinterpret_cast<uint32_t*>(base + s.off_counters);
+  p.best = s.off_best ? reinterpret_cast<unsigned long long*>(base + s.off_best) : nullptr;
+  p.done = s.off_done ? reinterpret_cast<uint32_t*>(base + s.off_done) : nullptr;
+  p.tiles = s.tiles;
+  p.iters = s.iters;
+  p.total = s.total;
+  p.workers = s.workers;
+}
+
+int32_t launch(int fmt, int epi, const vq::GemmParams& p, void* stream) {
+  const int err = vq::launch_gemm(fmt, epi, p, stream);
+  if (err != 0) return fail(VQ_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));
+  return VQ_OK;
+}
+
+}  // namespace
+
+namespace vq {
+
+Schedule make_schedule(int epi, int32_t n_out, int32_t k) {
+  Schedule s{};
+  const int64_t cols_per_tile = epi == EPI_SILU ? kSubRows : (int64_t)kSubRows * kNT;
+  s.tiles = (int32_t)((n_out + cols_per_tile - 1) / cols_per_tile);
+  s.iters = k / kIterK;
+  s.total = (int64_t)s.tiles * s.iters;
+  int64_t w = (s.total + kMinItersPerWorker - 1) / kMinItersPerWorker;
+  if (w > kMaxWorkers) w = kMaxWorkers;
+  if (w < 1) w = 1;
+  s.workers = (int32_t)w;
+  size_t off = 0;
+  s.off_partials = off;
+  off = align_up(off + (size_t)2 * s.workers * kSlotFloats * sizeof(float), 256);
+  s.off_counters = off;
+  off = align_up(off + (size_t)s.tiles * sizeof(uint32_t), 256);
+  if (epi == EPI_ARGMAX) {
+    s.off_best = off;
+    off = align_up(off + (size_t)kBuckets * kMaxRows * sizeof(unsigned long long), 256);
+    s.off_done = off;
+    off = align_up(off + sizeof(uint32_t), 256);
+  }
+  s.bytes = off;
+  return s;
+}
+
+}  // namespace vq
+
+extern "C" {
+
+int32_t vq_abi_version(void) { return VQ_ABI_VERSION; }
+
+const char* vq_last_error(void) { return g_last_error.c_str(); }
+
+const char* vq_status_str(int32_t s) {
+  switch (s) {
+    case VQ_OK: return "VQ_OK";
+    case VQ_ERR_NULL: return "VQ_ERR_NULL";
+    case VQ_ERR_SHAPE: return "VQ_ERR_SHAPE";
+    case VQ_ERR_ALIGN: return "VQ_ERR_ALIGN";
+    case VQ_ERR_WORKSPACE: return "VQ_ERR_WORKSPACE";
+    case VQ_ERR_DEVICE: return "VQ_ERR_DEVICE";
+    case VQ_ERR_LAUNCH: return "VQ_ERR_LAUNCH";
+    case VQ_ERR_VALUE: return "VQ_ERR_VALUE";
+    default: return "VQ_ERR_UNKNOWN";
+  }
+}
+
+size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K) {
+  if (!shape_ok(M, N, K)) return 0;
+  switch (op) {
+    case VQ_OP_NVFP4: return vq::make_schedule(vq::EPI_NONE, N, K).bytes;
+    case VQ_OP_NVFP4_SILU_MUL:
+      if (N > (1 << 29)) return 0;
+      return vq::make_schedule(vq::EPI_SILU, N, K).bytes;
+    case VQ_OP_FP8: return vq::make_schedule(vq::EPI_NONE, N, K).bytes;
+    case VQ_OP_LMHEAD: return vq::make_schedule(vq::EPI_ARGMAX, N, K).bytes;
+    default: return 0;
+  }
+}
+
+int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* codes, const uint8_t* scales, float tensor_scale, void* y,
+                      int32_t y_dtype, int32_t M, int32_t N, int32_t K, int32_t epilogue, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!x || !codes || !scales || !y) return fail(VQ_ERR_NULL, "vq_gemm_nvfp4: x, codes, scales and y are required");
+  if (y_dtype != VQ_OUT_BF16 && y_dtype != VQ_OUT_F32) return fail(VQ_ERR_VALUE, "unknown y_dtype %d", y_dtype);
+  if (epilogue != VQ_EPI_NONE && epilogue != VQ_EPI_SILU_MUL) return fail(VQ_ERR_VALUE, "unknown epilogue %d", epilogue);
+  int32_t st = check_shape(M, N, K);
+  if (st) return st;
+  if (epilogue == VQ_EPI_SILU_MUL && N > (1 << 29)) return fail(VQ_ERR_SHAPE, "N = %d too large for SILU_MUL", N);
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 16))
+    return fail(VQ_ERR_ALIGN, "x, codes and scales must be 16-byte aligned");
+  if (!aligned(y, y_dtype == VQ_OUT_F32 ? 4 : 2)) return fail(VQ_ERR_ALIGN, "y is not aligned to its element size");
+  const int epi = epilogue == VQ_EPI_SILU_MUL ? vq::EPI_SILU : vq::EPI_NONE;
+  const vq::Schedule s = vq::make_schedule(epi, N, K);
+  st = check_ws(s, workspace, workspace_bytes);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  vq::GemmParams p{};
+  p.x = x;
+  p.codes = codes;
+  p.scales = scales;
+  p.out_scale = tensor_scale;
+  p.y = y;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.y_f32 = y_dtype == VQ_OUT_F32;
+  bind_workspace(p, s, workspace);
+  return launch(vq::FMT_NVFP4, epi, p, stream);
+}
+
+int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, float w_scale, void* y, int32_t y_dtype, int32_t M,
+                    int32_t N, int32_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w || !y) return fail(VQ_ERR_NULL, "vq_gemm_fp8: x, w and y are required");
+  if (y_dtype != VQ_OUT_BF16 && y_dtype != VQ_OUT_F32) return fail(VQ_ERR_VALUE, "unknown y_dtype %d", y_dtype);
+  int32_t st = check_shape(M, N, K);
+  if (st) return st;
+  if (!aligned(x, 16) || !aligned(w, 16)) return fail(VQ_ERR_ALIGN, "x and w must be 16-byte aligned");
+  if (!aligned(y, y_dtype == VQ_OUT_F32 ? 4 : 2)) return fail(VQ_ERR_ALIGN, "y is not aligned to its element size");
+  const vq::Schedule s = vq::make_schedule(vq::EPI_NONE, N, K);
+  st = check_ws(s, workspace, workspace_bytes);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  vq::GemmParams p{};
+  p.x = x;
+  p.codes = w;
+  p.out_scale = w_scale;
+  p.y = y;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.y_f32 = y_dtype == VQ_OUT_F32;
+  bind_workspace(p, s, workspace);
+  return launch(vq::FMT_FP8, vq::EPI_NONE, p, stream);
+}
+
+int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* codes, const uint8_t* scales, float tensor_scale,
+                                const int32_t* draft, int32_t lanes, int32_t R, int32_t V, int32_t K,
+                                int32_t* argmax_out, float* maxlogit_out, int32_t* accept_len_out,
+                                int32_t* commit_out, void* logits_out, int32_t logits_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!h || !codes || !scales || !argmax_out || !accept_len_out)
+    return fail(VQ_ERR_NULL, "vq_lmhead_argmax_accept: h, codes, scales, argmax_out and accept_len_out are required");
+  if (R > 1 && !draft) return fail(VQ_ERR_NULL, "draft is required when R > 1");
+  if (lanes < 1 || lanes > 4) return fail(VQ_ERR_SHAPE, "lanes = %d outside [1, 4]", lanes);
+  if (R < 1 || R > 8) return fail(VQ_ERR_SHAPE, "R = %d outside [1, 8]", R);
+  if (logits_out && logits_dtype != VQ_OUT_BF16 && logits_dtype != VQ_OUT_F32)
+    return fail(VQ_ERR_VALUE, "unknown logits_dtype %d", logits_dtype);
+  const int32_t M = lanes * R;
+  int32_t st = check_shape(M, V, K);
+  if (st) return st;
+  if (!aligned(h, 16) || !aligned(codes, 16) || !aligned(scales, 16))
+    return fail(VQ_ERR_ALIGN, "h, codes and scales must be 16-byte aligned");
+  if (!aligned(argmax_out, 4) || !aligned(accept_len_out, 4) || (maxlogit_out && !aligned(maxlogit_out, 4)) ||
+      (commit_out && !aligned(commit_out, 4)) || (draft && !aligned(draft, 4)))
+    return fail(VQ_ERR_ALIGN, "int32/float arrays must be 4-byte aligned");
+  if (logits_out && !aligned(logits_out, logits_dtype == VQ_OUT_F32 ? 4 : 2))
+    return fail(VQ_ERR_ALIGN, "logits_out is not aligned to its element size");
+  const vq::Schedule s = vq::make_schedule(vq::EPI_ARGMAX, V, K);
+  st = check_ws(s, workspace, workspace_bytes);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  vq::GemmParams p{};
+  p.x = h;
+  p.codes = codes;
+  p.scales = scales;
+  p.out_scale = tensor_scale;
+  p.y = logits_out;
+  p.y_f32 = logits_dtype == VQ_OUT_F32;
+  p.M = M;
+  p.N = V;
+  p.K = K;
+  p.draft = draft;
+  p.lanes = lanes;
+  p.R = R;
+  p.argmax_out = argmax_out;
+  p.maxlogit_out = maxlogit_out;
+  p.accept_len_out = accept_len_out;
+  p.commit_out = commit_out;
+  bind_workspace(p, s, workspace);
+  return launch(vq::FMT_NVFP4, vq::EPI_ARGMAX, p, stream);
+}
+
+int32_t vq_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return fail(VQ_ERR_NULL, "vq_probe_copy: src and dst are required");
+  if (bytes == 0 || bytes % 16) return fail(VQ_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(VQ_ERR_ALIGN, "src and dst must be 16-byte aligned");
+  int32_t st = check_device();
+  if (st) return st;
+  const int err = vq::launch_probe_copy(src, dst, bytes, stream);
+  if (err) return fail(VQ_ERR_LAUNCH, "probe launch failed: %s", hipGetErrorString((hipError_t)err));
+  return VQ_OK;
+}
+
+int32_t vq_probe_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return fail(VQ_ERR_NULL, "vq_probe_read: src and sink are required");
+  if (bytes == 0 || bytes % 16) return fail(VQ_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  if (!aligned(src, 16) || !aligned(sink, 16)) return fail(VQ_ERR_ALIGN, "src and sink must be 16-byte aligned");
+  int32_t st = check_device();
+  if (st) return st;
+  const int err = vq::launch_probe_read(src, bytes, sink, stream);
+  if (err) return fail(VQ_ERR_LAUNCH, "probe launch failed: %s", hipGetErrorString((hipError_t)err));
+  return VQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,221 @@
+"""Thin Python binding of libverify (include/libverify.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, checks dtype/shape/contiguity, and passes raw device
+pointers and the current HIP stream to the C ABI. All arithmetic runs in the
+HIP kernels of libverify.so; there is no fallback of any kind, and a missing
+library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "lib", "libverify.so")
+
+VQ_OK = 0
+VQ_ERR_NULL = 1
+VQ_ERR_SHAPE = 2
+VQ_ERR_ALIGN = 3
+VQ_ERR_WORKSPACE = 4
+VQ_ERR_DEVICE = 5
+VQ_ERR_LAUNCH = 6
+VQ_ERR_VALUE = 7
+
+VQ_OUT_BF16 = 0
+VQ_OUT_F32 = 1
+VQ_EPI_NONE = 0
+VQ_EPI_SILU_MUL = 1
+VQ_OP_NVFP4 = 0
+VQ_OP_NVFP4_SILU_MUL = 1
+VQ_OP_FP8 = 2
+VQ_OP_LMHEAD = 3
+
+EXPORTS = [
+    "vq_gemm_nvfp4", "vq_gemm_fp8", "vq_lmhead_argmax_accept", "vq_workspace_bytes",
+    "vq_status_str", "vq_last_error", "vq_abi_version", "vq_probe_copy", "vq_probe_read",
+]
+
+
+class VerifyError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_str(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libverify.so (built in-tree by bit_block_scaled_vq_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libverify.so is not built ({LIB_PATH}); run `python -m bit_block_scaled_vq_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    L.vq_gemm_nvfp4.argtypes = [vp, vp, vp, f32, vp, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.vq_gemm_nvfp4.restype = i32
+    L.vq_gemm_fp8.argtypes = [vp, vp, f32, vp, i32, i32, i32, i32, vp, sz, vp]
+    L.vq_gemm_fp8.restype = i32
+    L.vq_lmhead_argmax_accept.argtypes = [vp, vp, vp, f32, vp, i32, i32, i32, i32,
+                                          vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.vq_lmhead_argmax_accept.restype = i32
+    L.vq_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.vq_workspace_bytes.restype = sz
+    L.vq_status_str.argtypes = [i32]
+    L.vq_status_str.restype = ctypes.c_char_p
+    L.vq_last_error.argtypes = []
+    L.vq_last_error.restype = ctypes.c_char_p
+    L.vq_abi_version.argtypes = []
+    L.vq_abi_version.restype = i32
+    L.vq_probe_copy.argtypes = [vp, vp, sz, vp]
+    L.vq_probe_copy.restype = i32
+    L.vq_probe_read.argtypes = [vp, sz, vp, vp]
+    L.vq_probe_read.restype = i32
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().vq_status_str(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().vq_last_error().decode()
+
+
+def _check(status: int):
+    if status != VQ_OK:
+        raise VerifyError(status, last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtypes, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def _out_dtype(t) -> int:
+    torch = _torch()
+    return VQ_OUT_F32 if t.dtype == torch.float32 else VQ_OUT_BF16
+
+
+def workspace_bytes(op: int, M: int, N: int, K: int) -> int:
+    return int(lib().vq_workspace_bytes(op, M, N, K))
+
+
+def workspace(op: int, M: int, N: int, K: int, device="cuda"):
+    """A zero-filled workspace for `op` (reusable across stream-ordered calls)."""
+    torch = _torch()
+    n = workspace_bytes(op, M, N, K)
+    if n == 0:
+        raise VerifyError(VQ_ERR_SHAPE, f"invalid shape for workspace: M={M} N={N} K={K}")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def vq_gemm_nvfp4(x, codes, scales, tensor_scale: float, y, epilogue: int = VQ_EPI_NONE,
+                  workspace=None, stream=None):
+    """y[M][N] = x . W^T (NVFP4 W), or silu(gate)*up for VQ_EPI_SILU_MUL."""
+    torch = _torch()
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(codes, "codes", (torch.uint8,), 2)
+    _need(scales, "scales", (torch.uint8,), 2)
+    _need(y, "y", (torch.bfloat16, torch.float32), 2)
+    M, K = x.shape
+    N = y.shape[1]
+    nw = 2 * N if epilogue == VQ_EPI_SILU_MUL else N
+    if y.shape[0] != M or tuple(codes.shape) != (nw, K // 2) or tuple(scales.shape) != (nw, K // 16):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)} codes {tuple(codes.shape)} "
+                         f"scales {tuple(scales.shape)} y {tuple(y.shape)}")
+    ws_ptr, ws_n = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    _check(lib().vq_gemm_nvfp4(_ptr(x), _ptr(codes), _ptr(scales), float(tensor_scale), _ptr(y),
+                               _out_dtype(y), M, N, K, int(epilogue), ws_ptr, ws_n, _stream(stream)))
+    return y
+
+
+def vq_gemm_fp8(x, w, w_scale: float, y, workspace=None, stream=None):
+    """y[M][N] = (x . E4M3(w)^T) * w_scale."""
+    torch = _torch()
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(w, "w", (torch.uint8,), 2)
+    _need(y, "y", (torch.bfloat16, torch.float32), 2)
+    M, K = x.shape
+    N = w.shape[0]
+    if tuple(y.shape) != (M, N) or w.shape[1] != K:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)} w {tuple(w.shape)} y {tuple(y.shape)}")
+    ws_ptr, ws_n = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    _check(lib().vq_gemm_fp8(_ptr(x), _ptr(w), float(w_scale), _ptr(y), _out_dtype(y), M, N, K,
+                             ws_ptr, ws_n, _stream(stream)))
+    return y
+
+
+def vq_lmhead_argmax_accept(h, codes, scales, tensor_scale: float, draft, lanes: int, R: int,
+                            argmax_out, accept_len_out, maxlogit_out=None, commit_out=None,
+                            logits_out=None, workspace=None, stream=None):
+    """Vocabulary head + per-row argmax + greedy accept (results stay on the device)."""
+    torch = _torch()
+    _need(h, "h", (torch.bfloat16,), 2)
+    _need(codes, "codes", (torch.uint8,), 2)
+    _need(scales, "scales", (torch.uint8,), 2)
+    _need(argmax_out, "argmax_out", (torch.int32,), 1)
+    _need(accept_len_out, "accept_len_out", (torch.int32,), 1)
+    if draft is not None:
+        _need(draft, "draft", (torch.int32,), 2)
+    if maxlogit_out is not None:
+        _need(maxlogit_out, "maxlogit_out", (torch.float32,), 1)
+    if commit_out is not None:
+        _need(commit_out, "commit_out", (torch.int32,), 2)
+    if logits_out is not None:
+        _need(logits_out, "logits_out", (torch.bfloat16, torch.float32), 2)
+    M, K = h.shape
+    V = codes.shape[0]
+    if M != lanes * R or tuple(codes.shape) != (V, K // 2) or tuple(scales.shape) != (V, K // 16):
+        raise ValueError("shape mismatch between h, lanes*R and the head")
+    if argmax_out.numel() != M or accept_len_out.numel() != lanes:
+        raise ValueError("output sizes do not match lanes and R")
+    if draft is not None and tuple(draft.shape) != (lanes, R - 1):
+        raise ValueError("draft must be [lanes][R-1]")
+    if commit_out is not None and tuple(commit_out.shape) != (lanes, R):
+        raise ValueError("commit_out must be [lanes][R]")
+    if logits_out is not None and tuple(logits_out.shape) != (M, V):
+        raise ValueError("logits_out must be [M][V]")
+    ws_ptr, ws_n = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    ld = _out_dtype(logits_out) if logits_out is not None else VQ_OUT_F32
+    _check(lib().vq_lmhead_argmax_accept(
+        _ptr(h), _ptr(codes), _ptr(scales), float(tensor_scale), _ptr(draft), lanes, R, V, K,
+        _ptr(argmax_out), _ptr(maxlogit_out), _ptr(accept_len_out), _ptr(commit_out),
+        _ptr(logits_out), ld, ws_ptr, ws_n, _stream(stream)))
+
+
+def vq_probe_copy(src, dst, stream=None):
+    _check(lib().vq_probe_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(), _stream(stream)))
+
+
+def vq_probe_read(src, sink, stream=None):
+    _check(lib().vq_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)))

@@ -1,0 +1,152 @@
+/* libverify -- weight stream of the speculative-decoding verify pass on MI355X (gfx950).
+ *
+ * The verify pass runs the target model once over the anchor plus the drafted
+ * tokens of each lane: an M x K activation block (M = 8 rows per lane, up to 4
+ * lanes) against every projection of the model, which makes each projection a
+ * skinny M x K x N GEMM rather than a GEMV ("144 tok/s needs 502 GB/s, and
+ * Apple sells two M5 Max chips", sections "The decode step is one command
+ * buffer" and "Why Apple silicon, and why not the M5"). The weights come in two
+ * formats ("lithos-metal: per-layer megakernels ...", sections "What one token
+ * costs the bus" and "Formats, and what runs where"):
+ *   - NVFP4: 4-bit E2M1 codes, one E4M3 block scale per 16 consecutive K
+ *     elements and one FP32 tensor scale that multiplies (9 bytes per 16
+ *     weights) -- the MLP projections and the vocabulary head;
+ *   - FP8 E4M3 codes with one FP32 per-tensor scale -- the Gated DeltaNet and
+ *     attention projections.
+ * Activations are bf16, accumulation is fp32 (weight-only quantisation).
+ * The pass ends in the vocabulary head, a per-row argmax and the greedy accept
+ * length ("lithos-metal ...", section "How DSpark is wired in").
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller; arrays are
+ *     dense and row-major. The library never allocates, frees, synchronises or
+ *     reads device memory on the host. Calls are asynchronous on `stream`
+ *     (a hipStream_t; NULL is the default stream) and can be captured into a
+ *     HIP graph.
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - NVFP4 layout: codes uint8 [rows][K/2], byte j of a row holds element
+ *     k = 2j in its low nibble and k = 2j+1 in its high nibble; scales uint8
+ *     [rows][K/16] (E4M3FN: no infinities, NaN = S.1111.111, max 448), scale
+ *     byte b covers k in [16b, 16b+16).
+ *   - Every argument is validated on the host before any HIP call; on error
+ *     nothing is launched and a non-zero vq_status is returned, with detail in
+ *     vq_last_error(). Shapes: 1 <= M <= 32, N >= 1, K >= 64 and K % 64 == 0.
+ *     x, h, codes, scales and w must be 16-byte aligned (every row then is);
+ *     y and logits must be aligned to their element size; int32/f32 arrays
+ *     4-byte aligned; the workspace 16-byte aligned.
+ *   - workspace: device memory of at least vq_workspace_bytes(op, M, N, K)
+ *     bytes, zero-filled by the caller ONCE before its first use. Kernels leave
+ *     every counter in it at zero again, so one workspace can be reused by
+ *     any number of stream-ordered calls (and graph replays). Two calls that
+ *     may run concurrently need distinct workspaces. A NULL or short workspace
+ *     returns VQ_ERR_WORKSPACE; the schedule never changes silently.
+ *   - Results are deterministic: the K partition and the order of the fixed
+ *     split-K reduction depend only on (N, K) and the epilogue, never
+ *     on M, so row r of an M-row call equals row r of any other M.
+ *   - The first call on a device checks that it is gfx950 (VQ_ERR_DEVICE).
+ *     A failed launch returns VQ_ERR_LAUNCH.
+ *   - Thread-safe; vq_last_error() is per host thread.
+ */
+#ifndef LIBVERIFY_H
+#define LIBVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VQ_ABI_VERSION 1
+
+typedef enum {
+  VQ_OK = 0,
+  VQ_ERR_NULL = 1,      /* a required pointer is NULL */
+  VQ_ERR_SHAPE = 2,     /* M, N, K, lanes, R or V out of range */
+  VQ_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
+  VQ_ERR_WORKSPACE = 4, /* workspace NULL or smaller than vq_workspace_bytes() */
+  VQ_ERR_DEVICE = 5,    /* no HIP device, or the current device is not gfx950 */
+  VQ_ERR_LAUNCH = 6,    /* the kernel launch failed */
+  VQ_ERR_VALUE = 7      /* an enum argument has an unknown value */
+} vq_status;
+
+typedef enum { VQ_OUT_BF16 = 0, VQ_OUT_F32 = 1 } vq_out_dtype;
+typedef enum { VQ_EPI_NONE = 0, VQ_EPI_SILU_MUL = 1 } vq_epilogue;
+typedef enum { VQ_OP_NVFP4 = 0, VQ_OP_NVFP4_SILU_MUL = 1, VQ_OP_FP8 = 2, VQ_OP_LMHEAD = 3 } vq_op;
+
+/* NVFP4 skinny GEMM: Y[M][N] = X[M][K] . W^T with
+ *   W[n][k] = E2M1(code[n][k]) * E4M3(scale[n][k/16]) * tensor_scale
+ * (formats: "lithos-metal ...", sections "What one token costs the bus" and
+ * "Formats, and what runs where"; 9 bytes per 16 weights).
+ *   x       bf16 [M][K]
+ *   codes   uint8 [Nw][K/2], scales uint8 [Nw][K/16]
+ *   epilogue VQ_EPI_NONE:     Nw = N, Y = X . W^T
+ *            VQ_EPI_SILU_MUL: Nw = 2N, rows [0,N) are the SwiGLU gate and rows
+ *            [N,2N) the up projection; Y = silu(gate) * up with silu(g) =
+ *            g / (1 + exp(-g)), computed in fp32 before the single rounding of
+ *            the store ("144 tok/s ...", section "The engine hard-codes the
+ *            model": SwiGLU gate, up, down).
+ *   y       [M][N], bf16 (round to nearest even) or fp32 per y_dtype.
+ * Returns a vq_status. */
+int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
+                      float tensor_scale, void* y, int32_t y_dtype,
+                      int32_t M, int32_t N, int32_t K, int32_t epilogue,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* FP8 skinny GEMM: Y[M][N] = (X[M][K] . E4M3(w)^T) * w_scale
+ * ("lithos-metal ...", section "What one token costs the bus": every Gated
+ * DeltaNet and attention projection is FP8 with a scalar scale).
+ *   x bf16 [M][K]; w uint8 [N][K] (E4M3FN codes); y [M][N] bf16 or fp32. */
+int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, float w_scale,
+                    void* y, int32_t y_dtype, int32_t M, int32_t N, int32_t K,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Vocabulary head + per-row argmax + greedy accept, all on the device
+ * ("Beating Splash on an M5 Max ...", section "What actually moved the
+ * needle": acceptance runs on the GPU and writes a small result block;
+ * "lithos-metal ...", section "How DSpark is wired in": the accept scan).
+ *   h       bf16 [M][K] hidden rows, M = lanes * R; rows l*R .. l*R+R-1
+ *           belong to lane l (row 0 of a lane follows its anchor token)
+ *   codes, scales, tensor_scale: the NVFP4 head W_head [V][K] (layout above)
+ *   draft   int32 [lanes][R-1]: draft j of lane l is compared with the argmax
+ *           of row l*R + j. Ids are not validated; an id outside [0,V) never
+ *           matches, and a row whose argmax is -1 matches no draft.
+ *   argmax_out     int32 [M]: lowest index among the equal maximal fp32 logits
+ *                  (-0 equals +0; NaN is never selected; -1 if a row has no
+ *                  non-NaN logit)
+ *   maxlogit_out   float [M] or NULL: the maximal logit (NaN for a -1 row)
+ *   accept_len_out int32 [lanes]: 1 + length of the matched draft prefix, in [1, R]
+ *   commit_out     int32 [lanes][R] or NULL: committed tokens (the argmax of
+ *                  rows 0..accept_len-1 of the lane), -1 after them
+ *   logits_out     [M][V] bf16 or fp32 per logits_dtype, or NULL
+ * Shapes: 1 <= lanes <= 4, 1 <= R <= 8, 1 <= V <= 2^30, K as above. */
+int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* codes, const uint8_t* scales,
+                                float tensor_scale, const int32_t* draft,
+                                int32_t lanes, int32_t R, int32_t V, int32_t K,
+                                int32_t* argmax_out, float* maxlogit_out,
+                                int32_t* accept_len_out, int32_t* commit_out,
+                                void* logits_out, int32_t logits_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by `op` at this shape (for VQ_OP_NVFP4_SILU_MUL, N is
+ * the output width, i.e. half the weight rows; for VQ_OP_LMHEAD, N = V and
+ * M = lanes * R). Returns 0 for an invalid shape. The size does not depend
+ * on M beyond the M <= 32 bound, so one workspace serves every M. */
+size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K);
+
+const char* vq_status_str(int32_t status);
+const char* vq_last_error(void);
+int32_t vq_abi_version(void);
+
+/* HBM probes used as the measured bandwidth denominator.
+ * vq_probe_copy: dst[i] = src[i] for `bytes` bytes (multiple of 16, both
+ * 16-byte aligned). vq_probe_read: reads `bytes` bytes of src and writes one
+ * 16-byte value derived from them to sink (keeps the reads live). */
+int32_t vq_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+int32_t vq_probe_read(const void* src, size_t bytes, void* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBVERIFY_H */

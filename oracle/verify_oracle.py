@@ -287,7 +287,8 @@ def greedy_accept(argmax_rows: np.ndarray, drafts: np.ndarray):
 
     Returns (accept_len[lanes], commit[lanes][R]) with commit[l][i] the
     committed token i (the target's argmax at row i) for i < accept_len and -1
-    after it.
+    after it. A row without a valid argmax (-1, all logits NaN) matches no
+    draft, so the scan stops there.
     """
     a = np.asarray(argmax_rows, dtype=np.int64)
     d = np.asarray(drafts, dtype=np.int64)
@@ -297,7 +298,7 @@ def greedy_accept(argmax_rows: np.ndarray, drafts: np.ndarray):
     commit = np.full((lanes, r), -1, dtype=np.int64)
     for l in range(lanes):
         acc = 0
-        while acc < r - 1 and a[l, acc] == d[l, acc]:
+        while acc < r - 1 and a[l, acc] >= 0 and a[l, acc] == d[l, acc]:
             acc += 1
         acc_len[l] = acc + 1
         commit[l, : acc + 1] = a[l, : acc + 1]

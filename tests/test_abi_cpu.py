@@ -1,0 +1,122 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call.
+
+No test here launches anything: every call either fails validation or, on a
+host without a GPU, stops at the device check. The one call that would pass
+validation is skipped when a GPU is visible.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_block_scaled_vq_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ops.LIB_PATH), reason="libverify.so not built")
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "libverify.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int32_t|size_t)\s+(vq_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    L = ops.lib()
+    names = _header_functions()
+    assert set(names) == set(ops.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    L = ops.lib()
+    assert L.vq_abi_version() == 1
+    assert ops.status_str(ops.VQ_OK) == "VQ_OK"
+    assert ops.status_str(ops.VQ_ERR_WORKSPACE) == "VQ_ERR_WORKSPACE"
+    assert ops.status_str(99) == "VQ_ERR_UNKNOWN"
+
+
+A = 1 << 20  # a fake, 16-byte-aligned address: never dereferenced (validation fails first)
+
+
+def _nvfp4(x=A, c=A, s=A, y=A, yd=0, M=8, N=1024, K=512, epi=0, ws=A, wsn=1 << 30):
+    return ops.lib().vq_gemm_nvfp4(x, c, s, 1.0, y, yd, M, N, K, epi, ws, wsn, None)
+
+
+def test_gemm_nvfp4_validation():
+    assert _nvfp4(x=None) == ops.VQ_ERR_NULL
+    assert _nvfp4(y=None) == ops.VQ_ERR_NULL
+    assert _nvfp4(M=0) == ops.VQ_ERR_SHAPE
+    assert _nvfp4(M=33) == ops.VQ_ERR_SHAPE
+    assert _nvfp4(N=0) == ops.VQ_ERR_SHAPE
+    assert _nvfp4(K=32) == ops.VQ_ERR_SHAPE
+    assert _nvfp4(K=96) == ops.VQ_ERR_SHAPE
+    assert _nvfp4(yd=5) == ops.VQ_ERR_VALUE
+    assert _nvfp4(epi=3) == ops.VQ_ERR_VALUE
+    assert _nvfp4(x=A + 8) == ops.VQ_ERR_ALIGN
+    assert _nvfp4(c=A + 4) == ops.VQ_ERR_ALIGN
+    assert _nvfp4(y=A + 1) == ops.VQ_ERR_ALIGN
+    assert _nvfp4(ws=None) == ops.VQ_ERR_WORKSPACE
+    assert _nvfp4(wsn=16) == ops.VQ_ERR_WORKSPACE
+    assert "workspace" in ops.last_error()
+
+
+def test_gemm_fp8_validation():
+    L = ops.lib()
+    assert L.vq_gemm_fp8(None, A, 1.0, A, 0, 8, 64, 64, A, 1 << 30, None) == ops.VQ_ERR_NULL
+    assert L.vq_gemm_fp8(A, A, 1.0, A, 0, 8, 64, 100, A, 1 << 30, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_gemm_fp8(A, A + 2, 1.0, A, 0, 8, 64, 64, A, 1 << 30, None) == ops.VQ_ERR_ALIGN
+    assert L.vq_gemm_fp8(A, A, 1.0, A, 0, 8, 64, 64, A, 0, None) == ops.VQ_ERR_WORKSPACE
+
+
+def _head(h=A, draft=A, lanes=1, R=8, V=1000, K=256, am=A, al=A, logits=None, ld=1, ws=A, wsn=1 << 30):
+    return ops.lib().vq_lmhead_argmax_accept(h, A, A, 1.0, draft, lanes, R, V, K, am, None, al, None,
+                                             logits, ld, ws, wsn, None)
+
+
+def test_lmhead_validation():
+    assert _head(h=None) == ops.VQ_ERR_NULL
+    assert _head(am=None) == ops.VQ_ERR_NULL
+    assert _head(draft=None) == ops.VQ_ERR_NULL
+    assert _head(lanes=0) == ops.VQ_ERR_SHAPE
+    assert _head(lanes=5) == ops.VQ_ERR_SHAPE
+    assert _head(R=9) == ops.VQ_ERR_SHAPE
+    assert _head(V=0) == ops.VQ_ERR_SHAPE
+    assert _head(am=A + 2) == ops.VQ_ERR_ALIGN
+    assert _head(logits=A, ld=7) == ops.VQ_ERR_VALUE
+    assert _head(wsn=8) == ops.VQ_ERR_WORKSPACE
+
+
+def test_workspace_bytes():
+    L = ops.lib()
+    assert L.vq_workspace_bytes(ops.VQ_OP_NVFP4, 0, 10, 64) == 0
+    assert L.vq_workspace_bytes(ops.VQ_OP_NVFP4, 8, 10, 60) == 0
+    assert L.vq_workspace_bytes(9, 8, 10, 64) == 0
+    for op in (ops.VQ_OP_NVFP4, ops.VQ_OP_NVFP4_SILU_MUL, ops.VQ_OP_FP8, ops.VQ_OP_LMHEAD):
+        sizes = {L.vq_workspace_bytes(op, m, 17408, 5120) for m in (1, 8, 16, 24, 32)}
+        assert len(sizes) == 1 and sizes.pop() > 0          # M-independent
+    assert L.vq_workspace_bytes(ops.VQ_OP_LMHEAD, 8, 248320, 5120) > L.vq_workspace_bytes(ops.VQ_OP_NVFP4, 8, 248320, 5120)
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="would pass validation and launch with fake pointers")
+def test_valid_call_without_gpu_reports_device_error():
+    assert _nvfp4() == ops.VQ_ERR_DEVICE
+    assert ops.lib().vq_probe_copy(A, A, 1024, None) == ops.VQ_ERR_DEVICE
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ops, "_lib", None)
+    monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        ops.lib()

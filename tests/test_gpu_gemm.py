@@ -1,0 +1,247 @@
+"""GPU parity of vq_gemm_nvfp4 / vq_gemm_fp8 against the fp64 oracle.
+
+Every case calls the HIP library through its C ABI (ops.py is argument
+marshalling only) and compares with the oracle element by element on the same
+seeded inputs. fp32-mode outputs are gated at max|gpu-oracle|/max|oracle| <=
+2e-3; bf16 stores must equal RNE of the fp32 store bitwise and may differ from
+RNE(oracle) only in the flip class.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from bit_block_scaled_vq_amd import inputs
+from tests.gpu_helpers import (bf16_to_bits, check_bf16_store, check_f32, say, to_dev_bf16, to_dev_u8,
+                               torch_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _ops():
+    from bit_block_scaled_vq_amd import ops
+    return ops
+
+
+def run_nvfp4(x_bits, codes, scales, ts, n_out, epi=0, out="both", ws=None):
+    torch, dev = torch_dev()
+    ops = _ops()
+    x = to_dev_bf16(x_bits)
+    c = to_dev_u8(codes)
+    s = to_dev_u8(scales)
+    m, k = x_bits.shape
+    op = ops.VQ_OP_NVFP4_SILU_MUL if epi else ops.VQ_OP_NVFP4
+    ws = ws if ws is not None else ops.workspace(op, m, n_out, k, dev)
+    y32 = torch.empty((m, n_out), dtype=torch.float32, device=dev)
+    ops.vq_gemm_nvfp4(x, c, s, ts, y32, epilogue=epi, workspace=ws)
+    res = {"f32": y32.cpu().numpy()}
+    if out == "both":
+        yb = torch.empty((m, n_out), dtype=torch.bfloat16, device=dev)
+        ops.vq_gemm_nvfp4(x, c, s, ts, yb, epilogue=epi, workspace=ws)
+        res["bf16"] = bf16_to_bits(yb)
+    torch.cuda.synchronize()
+    return res
+
+
+def run_fp8(x_bits, w, wscale, out="both"):
+    torch, dev = torch_dev()
+    ops = _ops()
+    x = to_dev_bf16(x_bits)
+    wd = to_dev_u8(w)
+    m, k = x_bits.shape
+    n = w.shape[0]
+    ws = ops.workspace(ops.VQ_OP_FP8, m, n, k, dev)
+    y32 = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ops.vq_gemm_fp8(x, wd, wscale, y32, workspace=ws)
+    res = {"f32": y32.cpu().numpy()}
+    if out == "both":
+        yb = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ops.vq_gemm_fp8(x, wd, wscale, yb, workspace=ws)
+        res["bf16"] = bf16_to_bits(yb)
+    torch.cuda.synchronize()
+    return res
+
+
+# ------------------------------------------------------------------- NVFP4
+
+def test_nvfp4_single_gemm_m8_k512_n1024():
+    say("case: NVFP4 M=8 K=512 N=1024 (seed 0 recipe)")
+    x = inputs.x_bf16((1,), 8, 512)
+    codes, scales = inputs.nvfp4_weights((1,), 1024, 512)
+    ref = O.gemm_nvfp4(x, codes, scales, 1.0)
+    r = run_nvfp4(x, codes, scales, 1.0, 1024)
+    check_f32(r["f32"], ref, what="cfg1 f32")
+    check_bf16_store(r["bf16"], r["f32"], ref)
+
+
+@pytest.mark.parametrize("m,n,k,ts", [
+    (1, 1, 64, 1.0), (3, 33, 192, 0.37), (8, 100, 512, 1.0), (13, 257, 320, 2.5),
+    (24, 64, 1024, 1.0), (32, 200, 256, 0.125), (8, 4096, 2048, 1.0), (5, 1000, 5120, 1.0),
+    (16, 2, 128, 1.0), (8, 65, 64, 1.0),
+])
+def test_nvfp4_shapes(m, n, k, ts):
+    say(f"case: NVFP4 M={m} N={n} K={k} ts={ts}")
+    x = inputs.x_bf16((100, m, n, k), m, k)
+    codes, scales = inputs.nvfp4_weights((100, m, n, k), n, k)
+    ref = O.gemm_nvfp4(x, codes, scales, ts)
+    r = run_nvfp4(x, codes, scales, ts, n)
+    check_f32(r["f32"], ref, what=f"M{m} N{n} K{k}")
+    check_bf16_store(r["bf16"], r["f32"], ref)
+
+
+def test_nvfp4_one_hot_is_bit_exact():
+    # Y[0, n] = W[n, k] * 1.0 exactly: pins the decode, the nibble order, the
+    # scale-block mapping and the operand roles.
+    n, k, ts = 130, 320, 0.75
+    codes, scales = inputs.nvfp4_weights((101,), n, k)
+    w = O.dequant_nvfp4(codes, scales, ts)
+    for kk in (0, 1, 7, 8, 15, 16, 31, 32, 63, 64, 100, 255, 256, 319):
+        say(f"case: one-hot k={kk}")
+        x = np.zeros((1, k), dtype=np.uint16)
+        x[0, kk] = 0x3F80
+        r = run_nvfp4(x, codes, scales, ts, n, out="f32")
+        assert np.array_equal(r["f32"][0].astype(np.float64), w[:, kk].astype(np.float32).astype(np.float64)), kk
+
+
+def test_nvfp4_special_values():
+    m, n, k = 4, 96, 256
+    x = inputs.x_bf16((102,), m, k)
+    codes, scales = inputs.nvfp4_weights((102,), n, k)
+    # zero block scales, NaN block scales on two rows, all-(-0) codes on a row
+    scales[:, 3] = 0
+    scales[5, 7] = 0x7F
+    scales[90, 0] = 0xFF
+    codes[10, :] = 0x88
+    scales[10, :] = 0x38  # 1.0
+    ref = O.gemm_nvfp4(x, codes, scales, 1.0)
+    r = run_nvfp4(x, codes, scales, 1.0, n)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(r["f32"]), nan_ref)
+    assert nan_ref[:, 5].all() and nan_ref[:, 90].all()
+    fin = ~nan_ref
+    check_f32(np.where(fin, r["f32"], 0), np.where(fin, ref, 0), what="finite part")
+    assert np.all(r["f32"][:, 10] == 0.0)
+
+
+def test_nvfp4_silu_mul_small():
+    m, inter, k = 8, 300, 512
+    x = inputs.x_bf16((103,), m, k)
+    codes, scales = inputs.nvfp4_weights((103,), 2 * inter, k)
+    h, hb = O.mlp_silu_mul(x, codes, scales, 1.0, inter)
+    r = run_nvfp4(x, codes, scales, 1.0, inter, epi=1)
+    check_f32(r["f32"], h, what="silu*up f32")
+    check_bf16_store(r["bf16"], r["f32"], h)
+
+
+def test_mlp_layer_m8_full_size():
+    say("case: MLP layer M=8: [gate;up] 34816x5120 + SiLU*up, down 5120x17408")
+    m, hid, inter = 8, 5120, 17408
+    x = inputs.x_bf16((2,), m, hid)
+    gu_c, gu_s = inputs.nvfp4_weights((2, 0), 2 * inter, hid)
+    dn_c, dn_s = inputs.nvfp4_weights((2, 1), hid, inter)
+    h_ref, h_bits = O.mlp_silu_mul(x, gu_c, gu_s, 1.0, inter)
+    r1 = run_nvfp4(x, gu_c, gu_s, 1.0, inter, epi=1)
+    check_f32(r1["f32"], h_ref, what="h = silu(gate)*up")
+    check_bf16_store(r1["bf16"], r1["f32"], h_ref)
+    # down projection on the GPU's own bf16 h and, for the oracle, the same bits
+    y_ref = O.gemm_nvfp4(r1["bf16"], dn_c, dn_s, 1.0)
+    r2 = run_nvfp4(r1["bf16"], dn_c, dn_s, 1.0, hid)
+    check_f32(r2["f32"], y_ref, what="down")
+    check_bf16_store(r2["bf16"], r2["f32"], y_ref)
+    # and the whole layer against the oracle's own chain (h rounded once to bf16)
+    y_chain = O.gemm_nvfp4(h_bits, dn_c, dn_s, 1.0)
+    check_f32(r2["f32"], y_chain, what="layer vs oracle chain")
+
+
+# --------------------------------------------------------------------- FP8
+
+@pytest.mark.parametrize("m,n,k,ws", [
+    (1, 1, 64, 1.0), (8, 100, 512, 0.37), (13, 257, 320, 0.125), (32, 64, 1024, 1.0), (8, 1000, 6144, 1.0),
+])
+def test_fp8_shapes(m, n, k, ws):
+    say(f"case: FP8 M={m} N={n} K={k} scale={ws}")
+    x = inputs.x_bf16((104, m, n, k), m, k)
+    w = inputs.fp8_weights((104, m, n, k), n, k)
+    ref = O.gemm_fp8(x, w, ws)
+    r = run_fp8(x, w, ws)
+    check_f32(r["f32"], ref, what=f"fp8 M{m} N{n} K{k}")
+    check_bf16_store(r["bf16"], r["f32"], ref)
+
+
+def test_fp8_all_codes_one_hot():
+    # every E4M3 code (NaN codes included) decoded exactly by the kernel
+    n, k = 256, 64
+    w = np.zeros((n, k), dtype=np.uint8)
+    w[:, 5] = np.arange(256, dtype=np.uint8)
+    x = np.zeros((1, k), dtype=np.uint16)
+    x[0, 5] = 0x3F80
+    r = run_fp8(x, w, 1.0, out="f32")
+    ref = O.E4M3FN_TABLE
+    got = r["f32"][0].astype(np.float64)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+# ---------------------------------------------- properties of the schedule
+
+def test_rows_independent_of_m_and_deterministic():
+    torch, dev = torch_dev()
+    ops = _ops()
+    n, k = 5120, 17408        # the narrow, long-K down projection shape
+    codes, scales = inputs.nvfp4_weights((105,), n, k)
+    x32 = inputs.x_bf16((105,), 32, k)
+    c, s = to_dev_u8(codes), to_dev_u8(scales)
+    ws = ops.workspace(ops.VQ_OP_NVFP4, 32, n, k, dev)
+    outs = {}
+    for m in (32, 8, 1, 24, 16):
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        ops.vq_gemm_nvfp4(to_dev_bf16(x32[:m]), c, s, 1.0, y, workspace=ws)
+        outs[m] = y.cpu().numpy()
+    for m in (8, 1, 24, 16):
+        assert np.array_equal(outs[m], outs[32][:m]), m
+    y2 = torch.empty((32, n), dtype=torch.float32, device=dev)
+    ops.vq_gemm_nvfp4(to_dev_bf16(x32), c, s, 1.0, y2, workspace=ws)
+    assert np.array_equal(y2.cpu().numpy(), outs[32])
+    ref = O.gemm_nvfp4(x32[:8], codes, scales, 1.0)
+    check_f32(outs[8], ref, what="down M=8")
+
+
+def test_graph_capture_and_replay():
+    torch, dev = torch_dev()
+    ops = _ops()
+    m, n, k = 8, 2048, 1024
+    x = inputs.x_bf16((106,), m, k)
+    codes, scales = inputs.nvfp4_weights((106,), n, k)
+    xd, c, s = to_dev_bf16(x), to_dev_u8(codes), to_dev_u8(scales)
+    ws = ops.workspace(ops.VQ_OP_NVFP4, m, n, k, dev)
+    y_eager = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ops.vq_gemm_nvfp4(xd, c, s, 1.0, y_eager, workspace=ws)
+    eager = y_eager.cpu().numpy()
+    y = torch.zeros((m, n), dtype=torch.float32, device=dev)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            ops.vq_gemm_nvfp4(xd, c, s, 1.0, y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(st)
+    for i in range(4):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), eager), i
+        ops.vq_gemm_nvfp4(xd, c, s, 1.0, y_eager, workspace=ws)  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_binding_rejects_short_workspace():
+    torch, dev = torch_dev()
+    ops = _ops()
+    x = torch.zeros((8, 512), dtype=torch.bfloat16, device=dev)
+    c = torch.zeros((1024, 256), dtype=torch.uint8, device=dev)
+    s = torch.zeros((1024, 32), dtype=torch.uint8, device=dev)
+    y = torch.empty((8, 1024), dtype=torch.float32, device=dev)
+    ws = torch.zeros(64, dtype=torch.uint8, device=dev)
+    with pytest.raises(ops.VerifyError) as ei:
+        ops.vq_gemm_nvfp4(x, c, s, 1.0, y, workspace=ws)
+    assert ei.value.status == ops.VQ_ERR_WORKSPACE
