@@ -77,15 +77,19 @@ class Pass:
         t0 = time.time()
         self.w = []
         for i, (kind, fmt, n, k) in enumerate(self.items):
+            # canonical weights are generated on the device, packed once (as at
+            # weight-load time) and dropped; the pass reads only packed weights
             key = (5, i)
             if fmt == "fp8":
-                self.w.append((inputs.device_fp8_weights(key, n, k, dev),))
+                self.w.append(ops.pack_fp8(inputs.device_fp8_weights(key, n, k, dev)))
             elif fmt == "nvfp4_silu":
-                self.w.append(inputs.device_nvfp4_weights(key, 2 * n, k, dev))
+                c, s = inputs.device_nvfp4_weights(key, 2 * n, k, dev)
+                self.w.append(ops.pack_nvfp4(c, s, gate_up=True))
             else:
-                self.w.append(inputs.device_nvfp4_weights(key, n, k, dev))
+                c, s = inputs.device_nvfp4_weights(key, n, k, dev)
+                self.w.append(ops.pack_nvfp4(c, s))
         torch.cuda.synchronize()
-        log(f"weights generated on device in {time.time() - t0:.1f}s")
+        log(f"weights generated and packed on device in {time.time() - t0:.1f}s")
         bf = torch.bfloat16
         self.x_hidden = inputs.device_x_bf16((5, 1000), M_ROWS, HIDDEN, dev)
         self.x_mix = inputs.device_x_bf16((5, 1001), M_ROWS, MIX_OUT_K, dev)
@@ -116,14 +120,14 @@ class Pass:
             y = self.y_in[:, :n] if n != HIDDEN else self.y_hid
             if n != HIDDEN:
                 y = self.y_in.view(-1)[: M_ROWS * n].view(M_ROWS, n)
-            ops.vq_gemm_fp8(x, w[0], 1.0, y, workspace=self.ws[(ops.VQ_OP_FP8, n, k)])
+            ops.vq_gemm_fp8(x, w, 1.0, y, workspace=self.ws[(ops.VQ_OP_FP8, n, k)])
         elif fmt == "nvfp4_silu":
-            ops.vq_gemm_nvfp4(self.x_hidden, w[0], w[1], 1.0, self.h_mlp, epilogue=ops.VQ_EPI_SILU_MUL,
+            ops.vq_gemm_nvfp4(self.x_hidden, w, 1.0, self.h_mlp, epilogue=ops.VQ_EPI_SILU_MUL,
                               workspace=self.ws[(ops.VQ_OP_NVFP4_SILU_MUL, n, k)])
         elif fmt == "nvfp4":
-            ops.vq_gemm_nvfp4(self.h_mlp, w[0], w[1], 1.0, self.y_hid, workspace=self.ws[(ops.VQ_OP_NVFP4, n, k)])
+            ops.vq_gemm_nvfp4(self.h_mlp, w, 1.0, self.y_hid, workspace=self.ws[(ops.VQ_OP_NVFP4, n, k)])
         else:
-            ops.vq_lmhead_argmax_accept(self.h_final, w[0], w[1], 1.0, self.drafts, 1, M_ROWS, self.argmax,
+            ops.vq_lmhead_argmax_accept(self.h_final, w, 1.0, n, self.drafts, 1, M_ROWS, self.argmax,
                                         self.accept, maxlogit_out=self.maxlogit, commit_out=self.commit,
                                         workspace=self.ws[(ops.VQ_OP_LMHEAD, n, k)])
 

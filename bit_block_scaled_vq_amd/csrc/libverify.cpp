@@ -76,8 +76,25 @@ int32_t check_ws(const vq::Schedule& s, void* ws, size_t ws_bytes) {
   return VQ_OK;
 }
 
+// Bytes of a packed matrix: kind VQ_PACK_*, `rows` canonical rows.
+size_t packed_bytes(int32_t kind, int64_t rows, int64_t k) {
+  if (rows < 1 || k < vq::kIterK || k % vq::kIterK != 0) return 0;
+  const int64_t iters = k / vq::kIterK;
+  if (kind == VQ_PACK_NVFP4) return (size_t)((rows + 63) / 64 * iters) * vq::kBlockF4;
+  if (kind == VQ_PACK_NVFP4_GATE_UP) return rows % 2 ? 0 : (size_t)((rows / 2 + 31) / 32 * iters) * vq::kBlockF4;
+  if (kind == VQ_PACK_FP8) return (size_t)((rows + 63) / 64 * iters) * vq::kBlockF8;
+  return 0;
+}
+
+int32_t check_w(const uint8_t* w, size_t w_bytes, size_t need) {
+  if (!aligned(w, 16)) return fail(VQ_ERR_ALIGN, "packed weights must be 16-byte aligned");
+  if (w_bytes < need) return fail(VQ_ERR_SHAPE, "packed weights have %zu bytes, this shape needs %zu", w_bytes, need);
+  return VQ_OK;
+}
+
 void bind_workspace(vq::GemmParams& p, const vq::Schedule& s, void* ws) {
   char* base = static_cast<char*>(ws);
+  p.zeros = reinterpret_cast<const uint16_t*>(base + s.off_zero);
   p.partials = reinterpret_cast<float*>(base + s.off_partials);
   p.counters = reinterpret_cast<uint32_t*>(base + s.off_counters);
   p.best = s.off_best ? reinterpret_cast<unsigned long long*>(base + s.off_best) : nullptr;
@@ -100,8 +117,7 @@ namespace vq {
 
 Schedule make_schedule(int epi, int32_t n_out, int32_t k) {
   Schedule s{};
-  const int64_t cols_per_tile = epi == EPI_SILU ? kSubRows : (int64_t)kSubRows * kNT;
-  s.tiles = (int32_t)((n_out + cols_per_tile - 1) / cols_per_tile);
+  s.tiles = tiles_for(epi, n_out);
   s.iters = k / kIterK;
   s.total = (int64_t)s.tiles * s.iters;
   int64_t w = (s.total + kMinItersPerWorker - 1) / kMinItersPerWorker;
@@ -109,6 +125,8 @@ Schedule make_schedule(int epi, int32_t n_out, int32_t k) {
   if (w < 1) w = 1;
   s.workers = (int32_t)w;
   size_t off = 0;
+  s.off_zero = off;
+  off += 256;
   s.off_partials = off;
   off = align_up(off + (size_t)2 * s.workers * kSlotFloats * sizeof(float), 256);
   s.off_counters = off;
@@ -158,19 +176,75 @@ size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K) {
   }
 }
 
-int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* codes, const uint8_t* scales, float tensor_scale, void* y,
+size_t vq_packed_bytes(int32_t kind, int32_t rows, int32_t K) { return packed_bytes(kind, rows, K); }
+
+int32_t vq_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, int32_t rows, int32_t K, int32_t gate_up,
+                      uint8_t* packed, size_t packed_bytes_avail, void* stream) {
+  if (!codes || !scales || !packed) return fail(VQ_ERR_NULL, "vq_pack_nvfp4: codes, scales and packed are required");
+  if (gate_up != 0 && gate_up != 1) return fail(VQ_ERR_VALUE, "gate_up must be 0 or 1");
+  const int32_t kind = gate_up ? VQ_PACK_NVFP4_GATE_UP : VQ_PACK_NVFP4;
+  if (rows < 1 || rows > (1 << 30) || (gate_up && rows % 2)) return fail(VQ_ERR_SHAPE, "rows = %d invalid", rows);
+  if (K < vq::kIterK || K % vq::kIterK != 0 || K > (1 << 24))
+    return fail(VQ_ERR_SHAPE, "K = %d must be a positive multiple of %d (at most 2^24)", K, vq::kIterK);
+  if (!aligned(codes, 16) || !aligned(scales, 16) || !aligned(packed, 16))
+    return fail(VQ_ERR_ALIGN, "codes, scales and packed must be 16-byte aligned");
+  const size_t need = packed_bytes(kind, rows, K);
+  if (packed_bytes_avail < need) return fail(VQ_ERR_SHAPE, "packed buffer has %zu bytes, %zu needed", packed_bytes_avail, need);
+  int32_t st = check_device();
+  if (st) return st;
+  vq::PackParams p{};
+  p.codes = codes;
+  p.scales = scales;
+  p.out = packed;
+  p.rows = rows;
+  p.K = K;
+  p.gate_up = gate_up;
+  p.tiles = gate_up ? (rows / 2 + 31) / 32 : (rows + 63) / 64;
+  p.iters = K / vq::kIterK;
+  const int err = vq::launch_pack(vq::FMT_NVFP4, p, stream);
+  if (err) return fail(VQ_ERR_LAUNCH, "pack launch failed: %s", hipGetErrorString((hipError_t)err));
+  return VQ_OK;
+}
+
+int32_t vq_pack_fp8(const uint8_t* w, int32_t rows, int32_t K, uint8_t* packed, size_t packed_bytes_avail,
+                    void* stream) {
+  if (!w || !packed) return fail(VQ_ERR_NULL, "vq_pack_fp8: w and packed are required");
+  if (rows < 1 || rows > (1 << 30)) return fail(VQ_ERR_SHAPE, "rows = %d invalid", rows);
+  if (K < vq::kIterK || K % vq::kIterK != 0 || K > (1 << 24))
+    return fail(VQ_ERR_SHAPE, "K = %d must be a positive multiple of %d (at most 2^24)", K, vq::kIterK);
+  if (!aligned(w, 16) || !aligned(packed, 16)) return fail(VQ_ERR_ALIGN, "w and packed must be 16-byte aligned");
+  const size_t need = packed_bytes(VQ_PACK_FP8, rows, K);
+  if (packed_bytes_avail < need) return fail(VQ_ERR_SHAPE, "packed buffer has %zu bytes, %zu needed", packed_bytes_avail, need);
+  int32_t st = check_device();
+  if (st) return st;
+  vq::PackParams p{};
+  p.codes = w;
+  p.out = packed;
+  p.rows = rows;
+  p.K = K;
+  p.tiles = (rows + 63) / 64;
+  p.iters = K / vq::kIterK;
+  const int err = vq::launch_pack(vq::FMT_FP8, p, stream);
+  if (err) return fail(VQ_ERR_LAUNCH, "pack launch failed: %s", hipGetErrorString((hipError_t)err));
+  return VQ_OK;
+}
+
+int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* w, size_t w_bytes, float tensor_scale, void* y,
                       int32_t y_dtype, int32_t M, int32_t N, int32_t K, int32_t epilogue, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  if (!x || !codes || !scales || !y) return fail(VQ_ERR_NULL, "vq_gemm_nvfp4: x, codes, scales and y are required");
+  if (!x || !w || !y) return fail(VQ_ERR_NULL, "vq_gemm_nvfp4: x, w and y are required");
   if (y_dtype != VQ_OUT_BF16 && y_dtype != VQ_OUT_F32) return fail(VQ_ERR_VALUE, "unknown y_dtype %d", y_dtype);
   if (epilogue != VQ_EPI_NONE && epilogue != VQ_EPI_SILU_MUL) return fail(VQ_ERR_VALUE, "unknown epilogue %d", epilogue);
   int32_t st = check_shape(M, N, K);
   if (st) return st;
   if (epilogue == VQ_EPI_SILU_MUL && N > (1 << 29)) return fail(VQ_ERR_SHAPE, "N = %d too large for SILU_MUL", N);
-  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 16))
-    return fail(VQ_ERR_ALIGN, "x, codes and scales must be 16-byte aligned");
+  if (!aligned(x, 16)) return fail(VQ_ERR_ALIGN, "x must be 16-byte aligned");
   if (!aligned(y, y_dtype == VQ_OUT_F32 ? 4 : 2)) return fail(VQ_ERR_ALIGN, "y is not aligned to its element size");
-  const int epi = epilogue == VQ_EPI_SILU_MUL ? vq::EPI_SILU : vq::EPI_NONE;
+  const bool silu = epilogue == VQ_EPI_SILU_MUL;
+  st = check_w(w, w_bytes, silu ? packed_bytes(VQ_PACK_NVFP4_GATE_UP, 2 * (int64_t)N, K)
+                                 : packed_bytes(VQ_PACK_NVFP4, N, K));
+  if (st) return st;
+  const int epi = silu ? vq::EPI_SILU : vq::EPI_NONE;
   const vq::Schedule s = vq::make_schedule(epi, N, K);
   st = check_ws(s, workspace, workspace_bytes);
   if (st) return st;
@@ -178,8 +252,7 @@ int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* codes, const uint8_t* sc
   if (st) return st;
   vq::GemmParams p{};
   p.x = x;
-  p.codes = codes;
-  p.scales = scales;
+  p.w = w;
   p.out_scale = tensor_scale;
   p.y = y;
   p.M = M;
@@ -190,14 +263,16 @@ int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* codes, const uint8_t* sc
   return launch(vq::FMT_NVFP4, epi, p, stream);
 }
 
-int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, float w_scale, void* y, int32_t y_dtype, int32_t M,
-                    int32_t N, int32_t K, void* workspace, size_t workspace_bytes, void* stream) {
+int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, size_t w_bytes, float w_scale, void* y, int32_t y_dtype,
+                    int32_t M, int32_t N, int32_t K, void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !w || !y) return fail(VQ_ERR_NULL, "vq_gemm_fp8: x, w and y are required");
   if (y_dtype != VQ_OUT_BF16 && y_dtype != VQ_OUT_F32) return fail(VQ_ERR_VALUE, "unknown y_dtype %d", y_dtype);
   int32_t st = check_shape(M, N, K);
   if (st) return st;
-  if (!aligned(x, 16) || !aligned(w, 16)) return fail(VQ_ERR_ALIGN, "x and w must be 16-byte aligned");
+  if (!aligned(x, 16)) return fail(VQ_ERR_ALIGN, "x must be 16-byte aligned");
   if (!aligned(y, y_dtype == VQ_OUT_F32 ? 4 : 2)) return fail(VQ_ERR_ALIGN, "y is not aligned to its element size");
+  st = check_w(w, w_bytes, packed_bytes(VQ_PACK_FP8, N, K));
+  if (st) return st;
   const vq::Schedule s = vq::make_schedule(vq::EPI_NONE, N, K);
   st = check_ws(s, workspace, workspace_bytes);
   if (st) return st;
@@ -205,7 +280,7 @@ int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, float w_scale, void* y,
   if (st) return st;
   vq::GemmParams p{};
   p.x = x;
-  p.codes = w;
+  p.w = w;
   p.out_scale = w_scale;
   p.y = y;
   p.M = M;
@@ -216,13 +291,13 @@ int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, float w_scale, void* y,
   return launch(vq::FMT_FP8, vq::EPI_NONE, p, stream);
 }
 
-int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* codes, const uint8_t* scales, float tensor_scale,
+int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* w, size_t w_bytes, float tensor_scale,
                                 const int32_t* draft, int32_t lanes, int32_t R, int32_t V, int32_t K,
                                 int32_t* argmax_out, float* maxlogit_out, int32_t* accept_len_out,
                                 int32_t* commit_out, void* logits_out, int32_t logits_dtype, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  if (!h || !codes || !scales || !argmax_out || !accept_len_out)
-    return fail(VQ_ERR_NULL, "vq_lmhead_argmax_accept: h, codes, scales, argmax_out and accept_len_out are required");
+  if (!h || !w || !argmax_out || !accept_len_out)
+    return fail(VQ_ERR_NULL, "vq_lmhead_argmax_accept: h, w, argmax_out and accept_len_out are required");
   if (R > 1 && !draft) return fail(VQ_ERR_NULL, "draft is required when R > 1");
   if (lanes < 1 || lanes > 4) return fail(VQ_ERR_SHAPE, "lanes = %d outside [1, 4]", lanes);
   if (R < 1 || R > 8) return fail(VQ_ERR_SHAPE, "R = %d outside [1, 8]", R);
@@ -231,13 +306,14 @@ int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* codes, const u
   const int32_t M = lanes * R;
   int32_t st = check_shape(M, V, K);
   if (st) return st;
-  if (!aligned(h, 16) || !aligned(codes, 16) || !aligned(scales, 16))
-    return fail(VQ_ERR_ALIGN, "h, codes and scales must be 16-byte aligned");
+  if (!aligned(h, 16)) return fail(VQ_ERR_ALIGN, "h must be 16-byte aligned");
   if (!aligned(argmax_out, 4) || !aligned(accept_len_out, 4) || (maxlogit_out && !aligned(maxlogit_out, 4)) ||
       (commit_out && !aligned(commit_out, 4)) || (draft && !aligned(draft, 4)))
     return fail(VQ_ERR_ALIGN, "int32/float arrays must be 4-byte aligned");
   if (logits_out && !aligned(logits_out, logits_dtype == VQ_OUT_F32 ? 4 : 2))
     return fail(VQ_ERR_ALIGN, "logits_out is not aligned to its element size");
+  st = check_w(w, w_bytes, packed_bytes(VQ_PACK_NVFP4, V, K));
+  if (st) return st;
   const vq::Schedule s = vq::make_schedule(vq::EPI_ARGMAX, V, K);
   st = check_ws(s, workspace, workspace_bytes);
   if (st) return st;
@@ -245,8 +321,7 @@ int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* codes, const u
   if (st) return st;
   vq::GemmParams p{};
   p.x = h;
-  p.codes = codes;
-  p.scales = scales;
+  p.w = w;
   p.out_scale = tensor_scale;
   p.y = logits_out;
   p.y_f32 = logits_dtype == VQ_OUT_F32;

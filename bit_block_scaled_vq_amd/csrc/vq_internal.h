@@ -9,18 +9,23 @@ namespace vq {
 enum Fmt : int { FMT_NVFP4 = 0, FMT_FP8 = 1 };
 enum Epi : int { EPI_NONE = 0, EPI_SILU = 1, EPI_ARGMAX = 2 };
 
-// Output columns handled by one tile: NT sub-tiles of 32 weight rows.
-constexpr int kSubRows = 32;
-constexpr int kNT = 2;
-// K consumed by one pipeline iteration of one wave.
-constexpr int kIterK = 64;
+// Packed weights are laid out in blocks of one tile (64 weight rows, four
+// sub-tiles of 16) by one k-iteration (128 K). NVFP4 block: 4 KB of codes +
+// 512 B of block scales; FP8 block: 8 KB.
+constexpr int kTileRows = 64;
+constexpr int kSub = 16;
+constexpr int kNT = 4;
+constexpr int kIterK = 128;
+constexpr int kBlockF4 = 4096 + 512;
+constexpr int kBlockF8 = 8192;
+
 // Stream-K workers (waves) per launch at most, and the minimum iterations a
 // worker gets before the worker count is reduced.
 constexpr int kMaxWorkers = 2048;
 constexpr int kMinItersPerWorker = 4;
-// Partial-sum slot: NT sub-tiles x 16 accumulator registers x 64 lanes (fp32).
+// Partial-sum slot: 4 sub-tiles x up to 16 accumulator registers x 64 lanes.
 constexpr int kSlotFloats = kNT * 16 * 64;
-// Argmax candidate buckets per row (spread the cross-tile atomics).
+// Argmax candidate buckets per row (spread the cross-worker atomics).
 constexpr int kBuckets = 64;
 constexpr int kMaxRows = 32;
 
@@ -29,22 +34,29 @@ struct Schedule {
   int32_t iters;      // I = K / kIterK
   int64_t total;      // T * I
   int32_t workers;    // P
-  size_t off_partials, off_counters, off_best, off_done, bytes;
+  size_t off_zero, off_partials, off_counters, off_best, off_done, bytes;
 };
 
-// The schedule depends only on (epilogue kind, N, K) -- never on M.
+// Tiles of an output of n_out columns: 64 columns per tile, or 32 with the
+// SiLU epilogue (whose tiles carry 32 gate + 32 up rows).
+inline int32_t tiles_for(int epi, int32_t n_out) {
+  const int32_t cols = epi == EPI_SILU ? kTileRows / 2 : kTileRows;
+  return (n_out + cols - 1) / cols;
+}
+
+// The schedule depends only on (epilogue kind, N, K), never on M.
 Schedule make_schedule(int epi, int32_t n_out, int32_t k);
 
 struct GemmParams {
   const uint16_t* x;
-  const uint8_t* codes;   // NVFP4 codes, or FP8 weights
-  const uint8_t* scales;  // NVFP4 block scales
+  const uint8_t* w;       // packed weights
   float out_scale;        // NVFP4 tensor scale or FP8 per-tensor scale
   void* y;
   int32_t M, N, K;        // N: output columns
   int32_t y_f32;
   int32_t tiles, iters, workers;
   int64_t total;
+  const uint16_t* zeros;  // 256 bytes the kernels never write (zero-filled with the workspace)
   float* partials;
   uint32_t* counters;
   unsigned long long* best;
@@ -57,8 +69,18 @@ struct GemmParams {
   int32_t* commit_out;
 };
 
+struct PackParams {
+  const uint8_t* codes;   // NVFP4 codes [rows][K/2] or FP8 weights [rows][K]
+  const uint8_t* scales;  // NVFP4 scales [rows][K/16]
+  uint8_t* out;
+  int32_t rows, K;        // rows of the canonical matrix
+  int32_t gate_up;        // NVFP4: tiles pair gate row r with up row r + rows/2
+  int32_t tiles, iters;
+};
+
 // Launchers: return 0 on success, else the hipError_t of the launch.
 int launch_gemm(int fmt, int epi, const GemmParams& p, void* stream);
+int launch_pack(int fmt, const PackParams& p, void* stream);
 int launch_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 int launch_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 

@@ -1,37 +1,42 @@
 // HIP kernels (gfx950 / CDNA4) for the weight stream of the speculative-decoding
-// verify pass: NVFP4 and FP8 E4M3 skinny GEMMs (M <= 32 rows) with a stream-K
-// schedule and a fixed-order split-K reduction, plus the vocabulary-head argmax
-// and greedy-accept epilogue, and two HBM probes.
+// verify pass: a one-time weight pack, NVFP4 and FP8 E4M3 skinny GEMMs
+// (M <= 32 rows) with a stream-K schedule and a fixed-order split-K reduction,
+// the vocabulary-head argmax + greedy-accept epilogue, and two HBM probes.
 //
 // Method: "lithos-metal: per-layer megakernels for Qwen3.8-27B on an M5 Max ..."
 // (sections "What one token costs the bus", "How DSpark is wired in",
-// "Formats, and what runs where"); "144 tok/s needs 502 GB/s ..." (section
-// "Why Apple silicon, and why not the M5": the verify rows form a real GEMM);
-// "Beating Splash on an M5 Max ..." (sections "The kernels were not the gap":
-// split-K on narrow projections; "What actually moved the needle": acceptance on
-// the GPU).
+// "Formats, and what runs where", and "The control experiment the blog leaves
+// out" for the idea of a weight layout packed for the bus); "144 tok/s needs
+// 502 GB/s ..." (section "Why Apple silicon, and why not the M5": the verify
+// rows form a real GEMM); "Beating Splash on an M5 Max ..." (sections "The
+// kernels were not the gap": split-K on narrow projections; "What actually
+// moved the needle": acceptance on the GPU).
 //
 // Design (MI355X-first, not the pages' Metal tiles):
-//  * Every wave is an independent stream-K worker. The work space is
-//    (tile, k-iteration); a tile is 2 x 32 weight rows, an iteration is 64 K.
-//    Worker w owns iterations [w*W/P, (w+1)*W/P), so all workers carry the same
-//    number of bytes and a GEMM has no tail wave. A tile split between workers
-//    is reduced by its last-arriving piece, in worker order (deterministic).
-//  * Weights stream straight from HBM into VGPRs with 16-byte non-temporal
-//    loads, several iterations in flight per wave.
-//  * The matrix unit is v_mfma_f32_32x32x16_bf16 with X as the A operand (rows
-//    = verify rows, padded to 32) and the decoded weights as B (32 columns).
-//    Its K of 16 is exactly one NVFP4 scale block, so each MFMA produces the
-//    unscaled block partial of 32 columns and the E4M3 block scale is applied
-//    after it with one fp32 FMA per useful accumulator. gfx950's packed fp4 ->
-//    bf16 convert only honours the exponent of its scale operand, so the scale
-//    cannot be folded into the decode; doing it after the MFMA costs about one
-//    VALU op per eight weights at M = 8.
-//  * Lanes load contiguous 16 bytes (32 codes = 2 blocks) of a row; one
-//    v_permlane32_swap per register pair regroups them so the two lanes that
-//    feed one MFMA column hold the two halves of the same block.
-//  * E2M1 and E4M3 decode use the hardware converts with a unit scale; both
-//    are exact in bf16.
+//  * Packed weights. A tile is 64 weight rows (four sub-tiles of 16), an
+//    iteration 128 K. The weights of one (tile, iteration) are one contiguous
+//    block, tiles in order, iterations in order inside a tile, arranged so that
+//    every wave load instruction reads 1 KB contiguous and lands exactly in the
+//    lanes that feed the MFMA (NVFP4: 4 KB of codes + 512 B of scales per
+//    block; FP8: 8 KB). A worker's stream is one linear read.
+//  * The matrix unit is v_mfma_f32_16x16x32_bf16: lane l gives A row l % 16
+//    and B column l % 16, both for k-group l / 16 (8 consecutive k); MFMA j of
+//    an iteration covers k [32j, 32j+32).
+//  * NVFP4: the E4M3 block scale is applied after the MFMA. The A operand holds
+//    each group of 8 activation rows twice: rows 0-7 carry X only on k-groups
+//    0,1 (= scale block 2j) and rows 8-15 only on k-groups 2,3 (= block 2j+1),
+//    zeros elsewhere. D rows 0-7 are then block 2j's partial sums and rows 8-15
+//    block 2j+1's, so every accumulator lane multiplies by exactly one block
+//    scale (one fp32 FMA) and lanes l, l+32 are added once per tile piece.
+//    gfx950's packed fp4 -> bf16 convert applies only the exponent of its
+//    scale operand, so a non-power-of-two E4M3 scale cannot be folded into it.
+//  * FP8: the MFMA accumulates directly; the per-tensor scale is applied in
+//    the epilogue.
+//  * Every wave is an independent stream-K worker over the (tile, iteration)
+//    space: worker w owns iterations [w*W/P, (w+1)*W/P). A tile split between
+//    workers is reduced by its last-arriving piece in worker order
+//    (deterministic). Cross-worker data moves only through agent-scope
+//    atomics, so no L2 write-back/invalidate is issued.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,20 +45,13 @@
 namespace vq {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ helpers
 
-__device__ __forceinline__ u32x4_t ld16_stream(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
-__device__ __forceinline__ uint32_t ld4_stream(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-}
-__device__ __forceinline__ u32x4_t ld16(const void* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
-}
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
 // 8 E2M1 codes (one dword, low nibble first) -> 8 bf16 in k order.
 __device__ __forceinline__ bf16x8_t dec_fp4x8(uint32_t w) {
@@ -83,12 +81,19 @@ __device__ __forceinline__ bf16x8_t dec_fp8x8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
+__device__ __forceinline__ float scale_byte(uint32_t w, int j) {
+  if (j == 0) return __builtin_amdgcn_cvt_f32_fp8(w, 0);
+  if (j == 1) return __builtin_amdgcn_cvt_f32_fp8(w, 1);
+  if (j == 2) return __builtin_amdgcn_cvt_f32_fp8(w, 2);
+  return __builtin_amdgcn_cvt_f32_fp8(w, 3);
+}
+
 // fp32 -> bf16 bits, round to nearest even; NaN -> quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x0040u;
+  return (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? quiet : rounded);
 }
 
 __device__ __forceinline__ void store_out(void* y, int f32, size_t idx, float v) {
@@ -122,151 +127,242 @@ __device__ __forceinline__ int64_t worker_of(int64_t it, int64_t total, int64_t 
   return ((it + 1) * workers - 1) / total;
 }
 
+// ------------------------------------------------------------- weight pack
+//
+// Canonical row of sub-tile t, sub-tile row n, of tile `tile` (-1: past the
+// matrix, packed as zeros). Plain: tile rows 64*tile .. +63. Gate/up pairs:
+// sub-tiles 0,1 hold gate rows 32*tile + 16t + n, sub-tiles 2,3 the up rows
+// half + 32*tile + 16(t-2) + n, half = rows / 2.
+__device__ __forceinline__ int pack_row(const PackParams& p, int tile, int t, int n) {
+  if (p.gate_up) {
+    const int half = p.rows / 2;
+    const int r = tile * 32 + (t & 1) * 16 + n;
+    return r < half ? r + (t >> 1) * half : -1;
+  }
+  const int r = tile * kTileRows + t * kSub + n;
+  return r < p.rows ? r : -1;
+}
+
+// One thread per 16-byte chunk of a packed NVFP4 block (288 chunks: 256 of
+// codes, 32 of scales). Codes chunk (t, l): lane l = 16g + n gets, for MFMA
+// j = 0..3, the 4 code bytes of k [128*it + 32j + 8g, +8) of row (t, n).
+// Scales chunk (h, n): byte 4t + j = scale of block 8*it + 2j + h of row (t, n).
+__device__ __forceinline__ void pack_nvfp4_chunk(const PackParams& p, int64_t gid) {
+  const int64_t blk = gid / 288;
+  const int c = (int)(gid - blk * 288);
+  const int tile = (int)(blk / p.iters), it = (int)(blk - (int64_t)tile * p.iters);
+  const size_t K = (size_t)p.K;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (c < 256) {
+    const int t = c >> 6, l = c & 63, n = l & 15, g = l >> 4;
+    const int r = pack_row(p, tile, t, n);
+    if (r >= 0) {
+      const uint8_t* row = p.codes + (size_t)r * (K / 2) + (size_t)it * 64 + g * 4;
+      v.x = *reinterpret_cast<const uint32_t*>(row);
+      v.y = *reinterpret_cast<const uint32_t*>(row + 16);
+      v.z = *reinterpret_cast<const uint32_t*>(row + 32);
+      v.w = *reinterpret_cast<const uint32_t*>(row + 48);
+    }
+  } else {
+    const int h = (c - 256) >> 4, n = (c - 256) & 15;
+    uint32_t words[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = pack_row(p, tile, t, n);
+      uint32_t wv = 0u;
+      if (r >= 0) {
+        const uint8_t* srow = p.scales + (size_t)r * (K / 16) + (size_t)it * 8 + h;
+        wv = (uint32_t)srow[0] | ((uint32_t)srow[2] << 8) | ((uint32_t)srow[4] << 16) | ((uint32_t)srow[6] << 24);
+      }
+      words[t] = wv;
+    }
+    v = u32x4_t{words[0], words[1], words[2], words[3]};
+  }
+  *reinterpret_cast<u32x4_t*>(p.out + blk * kBlockF4 + (size_t)c * 16) = v;
+}
+
+__global__ __launch_bounds__(256) void pack_nvfp4_kernel(PackParams p) {
+  const int64_t nchunks = (int64_t)p.tiles * p.iters * 288;
+  for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < nchunks;
+       gid += (int64_t)gridDim.x * blockDim.x)
+    pack_nvfp4_chunk(p, gid);
+}
+
+// One thread per 16-byte chunk of a packed FP8 block (512 chunks). Chunk
+// (t, h, l): lane l = 16g + n gets the 8 weights of k [128*it + 32j + 8g, +8)
+// for j = 2h and j = 2h+1 of row (t, n).
+__device__ __forceinline__ void pack_fp8_chunk(const PackParams& p, int64_t gid) {
+  const int64_t blk = gid / 512;
+  const int c = (int)(gid - blk * 512);
+  const int tile = (int)(blk / p.iters), it = (int)(blk - (int64_t)tile * p.iters);
+  const int t = c >> 7, h = (c >> 6) & 1, l = c & 63, n = l & 15, g = l >> 4;
+  const int r = pack_row(p, tile, t, n);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (r >= 0) {
+    const uint8_t* row = p.codes + (size_t)r * p.K + (size_t)it * kIterK + 64 * h + 8 * g;
+    const u32x2_t a = *reinterpret_cast<const u32x2_t*>(row);
+    const u32x2_t b = *reinterpret_cast<const u32x2_t*>(row + 32);
+    v = u32x4_t{a.x, a.y, b.x, b.y};
+  }
+  *reinterpret_cast<u32x4_t*>(p.out + blk * kBlockF8 + (size_t)c * 16) = v;
+}
+
+__global__ __launch_bounds__(256) void pack_fp8_kernel(PackParams p) {
+  const int64_t nchunks = (int64_t)p.tiles * p.iters * 512;
+  for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < nchunks;
+       gid += (int64_t)gridDim.x * blockDim.x)
+    pack_fp8_chunk(p, gid);
+}
+
+// ------------------------------------------------------------ kernel traits
+//
+// RG row groups: NVFP4 groups of 8 activation rows (each group's A operand is
+// the 16-row "two blocks" arrangement above), FP8 groups of 16 rows.
+
+template <int FMT, int RG>
+struct Traits {
+  static constexpr int REGS = 4 * RG;  // accumulator registers per sub-tile
+  static constexpr int RED = 16;       // lanes holding the same output rows
+  static __device__ __forceinline__ bool out_lane(int lane) { return FMT == FMT_FP8 || lane < 32; }
+  // output row of accumulator register (rg, r) of this lane
+  static __device__ __forceinline__ int row(int lane, int rg, int r) {
+    if (FMT == FMT_NVFP4) return 8 * rg + 4 * ((lane >> 4) & 1) + r;
+    return 16 * rg + 4 * (lane >> 4) + r;
+  }
+};
+
+template <int EPI>
+__device__ __forceinline__ int out_col(int tile, int t, int n) {
+  if (EPI == EPI_SILU) return tile * (kTileRows / 2) + (t & 1) * kSub + n;
+  return tile * kTileRows + t * kSub + n;
+}
+
 // ---------------------------------------------------------- per-iteration data
 
 template <int FMT>
-struct Buf;
-
+struct WBuf;
 template <>
-struct Buf<FMT_NVFP4> {
-  u32x4_t c[kNT];   // 16 code bytes per sub-tile row
-  uint32_t s[kNT];  // 4 block scales per sub-tile row
-  u32x4_t xa[4];    // X fragments of the 4 blocks (8 bf16 each)
+struct WBuf<FMT_NVFP4> {
+  u32x4_t c[kNT];  // per sub-tile: code dwords of MFMA steps 0..3
+  u32x4_t s;       // per sub-tile: the 4 block scales of this lane's half
+};
+template <>
+struct WBuf<FMT_FP8> {
+  u32x4_t c[kNT][2];  // per sub-tile: weights of MFMA steps (0,1) and (2,3)
+};
+template <int RG>
+struct XBuf {
+  u32x4_t xa[RG][4];  // X fragments of MFMA steps 0..3 per row group
 };
 
-template <>
-struct Buf<FMT_FP8> {
-  u32x4_t c[kNT][2];  // 2 x 16 weight bytes per sub-tile row
-  u32x4_t xa[4];
-};
-
-// Weight row of sub-tile t of tile `tile` for the lane's column n.
-template <int EPI>
-__device__ __forceinline__ int weight_row(const GemmParams& p, int tile, int t, int n) {
-  if (EPI == EPI_SILU) {
-    int col = tile * kSubRows + n;
-    col = col < p.N ? col : p.N - 1;
-    return col + t * p.N;
-  } else {
-    int row = tile * (kSubRows * kNT) + t * kSubRows + n;
-    return row < p.N ? row : p.N - 1;
-  }
-}
-
-template <int FMT, int EPI>
-__device__ __forceinline__ void load_iter(Buf<FMT>& b, const GemmParams& p, int tile, int kit,
-                                          int n, int g, bool xrow, int m) {
-  const size_t K = (size_t)p.K;
+template <int FMT>
+__device__ __forceinline__ void load_w(WBuf<FMT>& b, const uint8_t* blk, int lane) {
   if constexpr (FMT == FMT_NVFP4) {
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
-      const size_t row = (size_t)weight_row<EPI>(p, tile, t, n);
-      b.c[t] = ld16_stream(p.codes + row * (K / 2) + (size_t)kit * 32 + g * 16);
-      b.s[t] = ld4_stream(p.scales + row * (K / 16) + (size_t)kit * 4);
-    }
-    if (xrow) {
-      const uint16_t* xr = p.x + (size_t)m * K + (size_t)kit * kIterK + g * 8;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b.xa[j] = ld16(xr + 16 * j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b.xa[j] = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int t = 0; t < kNT; ++t) b.c[t] = ld16(blk + t * 1024 + lane * 16);
+    b.s = ld16(blk + 4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
   } else {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-      const size_t row = (size_t)weight_row<EPI>(p, tile, t, n);
-      const uint8_t* base = p.codes + row * K + (size_t)kit * kIterK + g * 16;
-      b.c[t][0] = ld16_stream(base);
-      b.c[t][1] = ld16_stream(base + 32);
-    }
-    if (xrow) {
-      const uint16_t* xr = p.x + (size_t)m * K + (size_t)kit * kIterK + g * 16;
-      b.xa[0] = ld16(xr);
-      b.xa[1] = ld16(xr + 8);
-      b.xa[2] = ld16(xr + 32);
-      b.xa[3] = ld16(xr + 40);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b.xa[j] = u32x4_t{0u, 0u, 0u, 0u};
+      b.c[t][0] = ld16(blk + (t * 2 + 0) * 1024 + lane * 16);
+      b.c[t][1] = ld16(blk + (t * 2 + 1) * 1024 + lane * 16);
     }
   }
 }
 
-// Accumulators: NVFP4 keeps the scaled sums in plain VGPRs (the MFMA output is
-// only a per-block temporary); FP8 accumulates inside the MFMA.
-template <int FMT, int MB>
-struct Acc;
-template <int MB>
-struct Acc<FMT_NVFP4, MB> {
-  float v[kNT][4 * MB];
+// X cursor: per row group a row pointer (or the zero region with a k-stride
+// of 0 for the NVFP4 lanes that must hold zeros).
+template <int FMT, int RG>
+struct XCursor {
+  const uint16_t* row[RG];
+  int kstep;
+  int jstep;
+  __device__ __forceinline__ void init(const GemmParams& p, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    bool carries = true;
+    if (FMT == FMT_NVFP4) carries = (i >> 3) == (g >> 1);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      int m = FMT == FMT_NVFP4 ? 8 * rg + (i & 7) : 16 * rg + i;
+      m = m < p.M ? m : p.M - 1;  // rows past M are padding: any valid row will do
+      row[rg] = carries ? p.x + (size_t)m * p.K + 8 * g : p.zeros;
+    }
+    kstep = carries ? kIterK : 0;
+    jstep = carries ? 32 : 0;
+  }
+  __device__ __forceinline__ void load(XBuf<RG>& b, int kit) const {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      const uint16_t* xr = row[rg] + (size_t)(kit * kstep);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b.xa[rg][j] = ld16(xr + j * jstep);
+    }
+  }
+};
+
+template <int FMT, int RG>
+struct Acc {
+  float v[kNT][4 * RG];
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4 * MB; ++r) v[t][r] = 0.0f;
+      for (int r = 0; r < 4 * RG; ++r) v[t][r] = 0.0f;
   }
   __device__ __forceinline__ float get(int t, int r) const { return v[t][r]; }
-};
-template <int MB>
-struct Acc<FMT_FP8, MB> {
-  f32x16_t v[kNT];
-  __device__ __forceinline__ void zero() {
+  // NVFP4: lanes l and l^32 hold the even- and odd-block halves of the sums.
+  __device__ __forceinline__ void combine() {
+    if constexpr (FMT == FMT_NVFP4) {
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) v[t] = f32x16_t{};
+      for (int t = 0; t < kNT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4 * RG; ++r) v[t][r] = v[t][r] + __shfl_xor(v[t][r], 32);
+    }
   }
-  __device__ __forceinline__ float get(int t, int r) const { return v[t][r]; }
 };
 
-template <int FMT, int MB>
-__device__ __forceinline__ void compute_iter(const Buf<FMT>& b, Acc<FMT, MB>& acc) {
+template <int FMT, int RG>
+__device__ __forceinline__ void compute_iter(const WBuf<FMT>& b, const XBuf<RG>& x, Acc<FMT, RG>& acc) {
   if constexpr (FMT == FMT_NVFP4) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-      // Lanes 0-31 hold blocks 0,1 of this iteration, lanes 32-63 blocks 2,3
-      // (each as two 8-code halves). The swap pairs half 0 (lanes 0-31) with
-      // half 1 (lanes 32-63) of the same block.
-      auto s02 = __builtin_amdgcn_permlane32_swap(b.c[t].x, b.c[t].y, false, false);
-      auto s13 = __builtin_amdgcn_permlane32_swap(b.c[t].z, b.c[t].w, false, false);
-      const uint32_t op[4] = {(uint32_t)s02[0], (uint32_t)s13[0], (uint32_t)s02[1], (uint32_t)s13[1]};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8_t wv = dec_fp4x8(op[j]);
-        const bf16x8_t xv = __builtin_bit_cast(bf16x8_t, b.xa[j]);
-        const f32x16_t d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xv, wv, f32x16_t{}, 0, 0, 0);
-        float sc;
-        if (j == 0) sc = __builtin_amdgcn_cvt_f32_fp8(b.s[t], 0);
-        else if (j == 1) sc = __builtin_amdgcn_cvt_f32_fp8(b.s[t], 1);
-        else if (j == 2) sc = __builtin_amdgcn_cvt_f32_fp8(b.s[t], 2);
-        else sc = __builtin_amdgcn_cvt_f32_fp8(b.s[t], 3);
+        const bf16x8_t wv = dec_fp4x8(b.c[t][j]);
+        const float sc = scale_byte(b.s[t], j);
 #pragma unroll
-        for (int r = 0; r < 4 * MB; ++r) acc.v[t][r] = __builtin_fmaf(sc, d[r], acc.v[t][r]);
+        for (int rg = 0; rg < RG; ++rg) {
+          const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[rg][j]), wv,
+                                                                    f32x4_t{}, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc.v[t][4 * rg + r] = __builtin_fmaf(sc, d[r], acc.v[t][4 * rg + r]);
+        }
       }
     }
   } else {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-      const bf16x8_t w0 = dec_fp8x8(b.c[t][0].x, b.c[t][0].y);
-      acc.v[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b.xa[0]), w0, acc.v[t], 0, 0, 0);
-      const bf16x8_t w1 = dec_fp8x8(b.c[t][0].z, b.c[t][0].w);
-      acc.v[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b.xa[1]), w1, acc.v[t], 0, 0, 0);
-      const bf16x8_t w2 = dec_fp8x8(b.c[t][1].x, b.c[t][1].y);
-      acc.v[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b.xa[2]), w2, acc.v[t], 0, 0, 0);
-      const bf16x8_t w3 = dec_fp8x8(b.c[t][1].z, b.c[t][1].w);
-      acc.v[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b.xa[3]), w3, acc.v[t], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4_t c = b.c[t][j >> 1];
+        const bf16x8_t wv = (j & 1) ? dec_fp8x8(c.z, c.w) : dec_fp8x8(c.x, c.y);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          f32x4_t a = {acc.v[t][4 * rg], acc.v[t][4 * rg + 1], acc.v[t][4 * rg + 2], acc.v[t][4 * rg + 3]};
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[rg][j]), wv, a, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc.v[t][4 * rg + r] = a[r];
+        }
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------- epilogues
 
-// Row of the output held by accumulator register r of a lane in half g.
-__device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
-
 // Final step of the head: reduce the bucketed candidates, write argmax / max,
 // run the greedy accept per lane and reset the workspace. One wave.
-__device__ __noinline__ void head_final(const GemmParams& p, int lane) {
-  __threadfence();
+__device__ __forceinline__ void head_final(const GemmParams& p, int lane) {
   int idx = -1;
   if (lane < p.M) {
     unsigned long long best = 0ull;
@@ -306,171 +402,262 @@ __device__ __noinline__ void head_final(const GemmParams& p, int lane) {
   if (lane == 0) __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int EPI, int MB, typename GetF>
-__device__ __forceinline__ void epilogue(const GemmParams& p, int tile, int lane, GetF get) {
-  const int n = lane & 31, g = lane >> 5;
+// Running per-lane argmax candidates of a worker (vocabulary head only).
+template <int REGS>
+struct Best {
+  unsigned long long k[REGS];
+};
+
+// Epilogue of a finished tile. NONE / SILU store the outputs; ARGMAX stores
+// the optional logits and folds the tile into the lane's running candidates.
+template <int FMT, int EPI, int RG, typename GetF>
+__device__ __forceinline__ void epilogue(const GemmParams& p, int tile, int lane, GetF get, Best<4 * RG>& best) {
+  using T = Traits<FMT, RG>;
+  if (!T::out_lane(lane)) return;
+  const int n = lane & 15;
   const float sc = p.out_scale;
-  if constexpr (EPI == EPI_NONE) {
 #pragma unroll
-    for (int r = 0; r < 4 * MB; ++r) {
-      const int m = acc_row(r, g);
-      if (m < p.M) {
+  for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = T::row(lane, rg, r);
+      const int q = 4 * rg + r;
+      if constexpr (EPI == EPI_NONE) {
+        if (m < p.M) {
+#pragma unroll
+          for (int t = 0; t < kNT; ++t) {
+            const int col = out_col<EPI>(tile, t, n);
+            if (col < p.N) store_out(p.y, p.y_f32, (size_t)m * p.N + col, get(t, q) * sc);
+          }
+        }
+      } else if constexpr (EPI == EPI_SILU) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int col = out_col<EPI>(tile, t, n);
+          if (m < p.M && col < p.N) {
+            const float gv = get(t, q) * sc;
+            const float uv = get(t + 2, q) * sc;
+            const float h = gv / (1.0f + expf(-gv)) * uv;
+            store_out(p.y, p.y_f32, (size_t)m * p.N + col, h);
+          }
+        }
+      } else {
 #pragma unroll
         for (int t = 0; t < kNT; ++t) {
-          const int col = tile * (kSubRows * kNT) + t * kSubRows + n;
-          if (col < p.N) store_out(p.y, p.y_f32, (size_t)m * p.N + col, get(t, r) * sc);
+          const int col = out_col<EPI>(tile, t, n);
+          const float v = get(t, q) * sc;
+          if (m < p.M && col < p.N) {
+            if (p.y) store_out(p.y, p.y_f32, (size_t)m * p.N + col, v);
+            const unsigned long long k = argmax_key(v, (uint32_t)col);
+            best.k[q] = k > best.k[q] ? k : best.k[q];
+          }
         }
       }
     }
-  } else if constexpr (EPI == EPI_SILU) {
-#pragma unroll
-    for (int r = 0; r < 4 * MB; ++r) {
-      const int m = acc_row(r, g);
-      const int col = tile * kSubRows + n;
-      if (m < p.M && col < p.N) {
-        const float gv = get(0, r) * sc;
-        const float uv = get(1, r) * sc;
-        const float h = gv / (1.0f + expf(-gv)) * uv;
-        store_out(p.y, p.y_f32, (size_t)m * p.N + col, h);
-      }
-    }
-  } else {
-    // Vocabulary head: optional logits, per-row candidate over this tile.
-#pragma unroll
-    for (int r = 0; r < 4 * MB; ++r) {
-      const int m = acc_row(r, g);
-      unsigned long long best = 0ull;
-#pragma unroll
-      for (int t = 0; t < kNT; ++t) {
-        const int col = tile * (kSubRows * kNT) + t * kSubRows + n;
-        const float v = get(t, r) * sc;
-        if (m < p.M && col < p.N) {
-          if (p.y) store_out(p.y, p.y_f32, (size_t)m * p.N + col, v);
-          const unsigned long long k = argmax_key(v, (uint32_t)col);
-          best = k > best ? k : best;
-        }
-      }
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) {
-        const unsigned long long o = __shfl_xor(best, off);
-        best = o > best ? o : best;
-      }
-      if (n == 0 && m < p.M && best != 0ull)
-        atomicMax(&p.best[(tile % kBuckets) * kMaxRows + m], best);
-    }
-    __threadfence();
-    uint32_t old = 0;
-    if (lane == 0) old = atomicAdd(p.done, 1u);
-    old = __shfl(old, 0);
-    if (old == (uint32_t)(p.tiles - 1)) head_final(p, lane);
   }
 }
 
-// End of a piece of tile `tile` held in `acc`. A tile covered by one worker is
-// finished directly; otherwise the piece is parked in its slot and the last
-// piece to arrive sums all pieces in worker order and finishes the tile.
-template <int FMT, int EPI, int MB>
-__device__ __forceinline__ void finish_piece(const GemmParams& p, int tile, bool full, int64_t w,
-                                             bool first, const Acc<FMT, MB>& acc, int lane) {
-  if (full) {
-    epilogue<EPI, MB>(p, tile, lane, [&](int t, int r) { return acc.get(t, r); });
-    return;
-  }
-  const int64_t slot = 2 * w + (first ? 0 : 1);
-  float* dst = p.partials + slot * kSlotFloats;
-#pragma unroll
-  for (int t = 0; t < kNT; ++t)
-#pragma unroll
-    for (int r = 0; r < 4 * MB; ++r) dst[(t * 16 + r) * 64 + lane] = acc.get(t, r);
-  __threadfence();
+// Cross-worker data (partial sums, counters, argmax candidates) only moves
+// through agent-scope atomics: relaxed atomic stores and loads are
+// write-through / coherent at device scope, so waiting for the stores'
+// acknowledgement before the counter increment orders them, and no L2
+// write-back or invalidate is needed.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// One piece of `tile` has been published; true when it was the last one, i.e.
+// the caller must reduce the pieces and finish the tile.
+__device__ __forceinline__ bool arrive(const GemmParams& p, int tile, int lane) {
   uint32_t old = 0;
-  if (lane == 0) old = atomicAdd(&p.counters[tile], 1u);
+  if (lane == 0) old = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0);
   const int64_t I = p.iters;
   const int64_t w0 = worker_of((int64_t)tile * I, p.total, p.workers);
   const int64_t w1 = worker_of((int64_t)(tile + 1) * I - 1, p.total, p.workers);
-  if (old != (uint32_t)(w1 - w0)) return;
-  __threadfence();
-  if (lane == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  float sum[kNT][4 * MB];
+  return old == (uint32_t)(w1 - w0);
+}
+
+template <int REGS>
+__device__ __forceinline__ void store_piece(const GemmParams& p, int64_t slot, int lane, const float (&v)[kNT][REGS]) {
+  static_assert(kNT * REGS * 64 <= kSlotFloats, "slot too small");
+  float* dst = p.partials + slot * kSlotFloats;
 #pragma unroll
   for (int t = 0; t < kNT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4 * MB; ++r) sum[t][r] = 0.0f;
+    for (int r = 0; r < REGS; ++r)
+      __hip_atomic_store(&dst[(t * REGS + r) * 64 + lane], v[t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum of every piece of `tile`, in worker order (deterministic).
+template <int REGS>
+__device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int lane, float (&sum)[kNT][REGS]) {
+  const int64_t I = p.iters;
+  const int64_t w0 = worker_of((int64_t)tile * I, p.total, p.workers);
+  const int64_t w1 = worker_of((int64_t)(tile + 1) * I - 1, p.total, p.workers);
+#pragma unroll
+  for (int t = 0; t < kNT; ++t)
+#pragma unroll
+    for (int r = 0; r < REGS; ++r) sum[t][r] = 0.0f;
   for (int64_t v = w0; v <= w1; ++v) {
     const bool vfirst = (worker_start(v, p.total, p.workers) / I) == tile;
     const float* src = p.partials + (2 * v + (vfirst ? 0 : 1)) * kSlotFloats;
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4 * MB; ++r) sum[t][r] += src[(t * 16 + r) * 64 + lane];
+      for (int r = 0; r < REGS; ++r)
+        sum[t][r] += __hip_atomic_load(&src[(t * REGS + r) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  epilogue<EPI, MB>(p, tile, lane, [&](int t, int r) { return sum[t][r]; });
+  if (lane == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // --------------------------------------------------------------- main kernel
 
-template <int FMT>
+// Iterations in flight per wave. The vector-memory counter retires loads in
+// issue order, so X fragments share the weights' ring (a shallower X ring
+// would cap the weight prefetch at its depth).
+template <int FMT, int RG>
 struct PipeDepth {
-  static constexpr int value = 4;
+  static constexpr int value = RG <= 2 ? 3 : 2;  // wide row groups: the X ring would spill
+};
+// Waves per SIMD: one row group keeps two waves per SIMD; more row groups keep
+// one wave per SIMD so the extra accumulators and X fragments stay in registers.
+template <int FMT, int RG>
+struct Occupancy {
+  static constexpr int value = RG == 1 ? 2 : 1;
 };
 
-// M <= 8 fits two waves per SIMD without spills; larger M keeps one wave per
-// SIMD so the extra accumulators stay in registers (AGPRs included).
-template <int FMT, int EPI, int MB>
-__global__ __launch_bounds__(256, MB == 1 ? 2 : 1) void vq_gemm_kernel(GemmParams p) {
-  constexpr int PD = PipeDepth<FMT>::value;
+template <int FMT, int EPI, int RG>
+__global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kernel(GemmParams p) {
+  using T = Traits<FMT, RG>;
+  constexpr int PD = PipeDepth<FMT, RG>::value;
+  constexpr int REGS = T::REGS;
+  constexpr size_t BLOCK = FMT == FMT_NVFP4 ? kBlockF4 : kBlockF8;
   const int lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (w >= p.workers) return;
   const int64_t s = worker_start(w, p.total, p.workers);
   const int64_t e = worker_start(w + 1, p.total, p.workers);
-  if (s >= e) return;
-  const int n = lane & 31, g = lane >> 5;
-  const int m = n;  // A-operand row of this lane
-  const bool xrow = m < p.M;
   const int I = p.iters;
 
-  Buf<FMT> buf[PD];
-  int ltile = (int)(s / I), lkit = (int)(s % I);
-  int64_t lit = s;
+  // The worker's weight stream is the contiguous run of blocks [s, e).
+  const uint8_t* wnext = p.w + (size_t)s * BLOCK;
+  XCursor<FMT, RG> xc;
+  xc.init(p, lane);
+  int xkit = (int)(s % I);
+  int64_t lit = s;  // next iteration to load
+
+  WBuf<FMT> wb[PD];
+  XBuf<RG> xb[PD];
+  auto load_next = [&](int q) {
+    load_w<FMT>(wb[q], wnext, lane);
+    xc.load(xb[q], xkit);
+    if (lit + 1 < e) {  // loads past the range re-read the last iteration
+      ++lit;
+      wnext += BLOCK;
+      if (++xkit == I) xkit = 0;
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < PD; ++q) load_next(q);
+
+  const int first_tile = (int)(s / I);
+  int ctile = first_tile;
+  int ckit = (int)(s - (int64_t)first_tile * I);
+  bool started_inside = ckit != 0;
+  bool have_head = false;
+  Acc<FMT, RG> acc;
+  acc.zero();
+  Best<REGS> best;
+#pragma unroll
+  for (int r = 0; r < REGS; ++r) best.k[r] = 0ull;
+  int finished = 0;  // tiles finished by this worker (vocabulary head)
+
+  auto tile_end = [&]() {
+    acc.combine();
+    if (!started_inside) {
+      epilogue<FMT, EPI, RG>(p, ctile, lane, [&](int t, int r) { return acc.get(t, r); }, best);
+      ++finished;
+    } else {
+      // the first tile was entered mid-way: park its piece now (published
+      // with the tail piece at the end of the range)
+      store_piece<REGS>(p, 2 * w, lane, acc.v);
+      have_head = true;
+    }
+    acc.zero();
+    started_inside = false;
+    ckit = 0;
+    ++ctile;
+  };
+
+  const int64_t count = e - s;
+  const int64_t blocks = count / PD;
+  for (int64_t bl = 0; bl < blocks; ++bl) {
+#pragma unroll
+    for (int q = 0; q < PD; ++q) {
+      compute_iter<FMT, RG>(wb[q], xb[q], acc);
+      load_next(q);
+      if (++ckit == I) tile_end();
+    }
+  }
+  const int rem = (int)(count - blocks * PD);
 #pragma unroll
   for (int q = 0; q < PD; ++q) {
-    if (lit < e) {
-      load_iter<FMT, EPI>(buf[q], p, ltile, lkit, n, g, xrow, m);
-      ++lit;
-      if (++lkit == I) { lkit = 0; ++ltile; }
+    if (q < rem) {
+      compute_iter<FMT, RG>(wb[q], xb[q], acc);
+      if (++ckit == I) tile_end();
     }
   }
 
-  int ctile = (int)(s / I), ckit = (int)(s % I);
-  const int first_tile = ctile;
-  int pstart = ckit;
-  int64_t cit = s;
-  Acc<FMT, MB> acc;
-  acc.zero();
-  while (cit < e) {
-#pragma unroll
-    for (int q = 0; q < PD; ++q) {
-      if (cit < e) {
-        compute_iter<FMT, MB>(buf[q], acc);
-        if (lit < e) {
-          load_iter<FMT, EPI>(buf[q], p, ltile, lkit, n, g, xrow, m);
-          ++lit;
-          if (++lkit == I) { lkit = 0; ++ltile; }
-        }
-        ++cit;
-        if (++ckit == I) {
-          finish_piece<FMT, EPI, MB>(p, ctile, pstart == 0, w, ctile == first_tile, acc, lane);
-          acc.zero();
-          ckit = 0;
-          pstart = 0;
-          ++ctile;
-        }
+  // Publish the partial pieces (the first tile if it was entered mid-way, the
+  // last tile if the range ends inside it), then finish every tile whose last
+  // piece this worker delivered.
+  const bool have_tail = ckit != 0;
+  if (have_head || have_tail) {
+    if (have_tail) {
+      acc.combine();
+      store_piece<REGS>(p, 2 * w + (ctile == first_tile ? 0 : 1), lane, acc.v);
+    }
+    wait_stores();
+    const bool last_head = have_head && arrive(p, first_tile, lane);
+    const bool last_tail = have_tail && arrive(p, ctile, lane);
+    if (last_head || last_tail) {
+      float sum[kNT][REGS];
+      if (last_head) {
+        reduce_tile<REGS>(p, first_tile, lane, sum);
+        epilogue<FMT, EPI, RG>(p, first_tile, lane, [&](int t, int r) { return sum[t][r]; }, best);
+        ++finished;
+      }
+      if (last_tail) {
+        reduce_tile<REGS>(p, ctile, lane, sum);
+        epilogue<FMT, EPI, RG>(p, ctile, lane, [&](int t, int r) { return sum[t][r]; }, best);
+        ++finished;
       }
     }
   }
-  if (ckit != 0) finish_piece<FMT, EPI, MB>(p, ctile, false, w, ctile == first_tile, acc, lane);
+
+  if constexpr (EPI == EPI_ARGMAX) {
+    if (finished > 0) {
+#pragma unroll
+      for (int q = 0; q < REGS; ++q) {
+        unsigned long long k = T::out_lane(lane) ? best.k[q] : 0ull;
+#pragma unroll
+        for (int off = T::RED / 2; off >= 1; off >>= 1) {
+          const unsigned long long o = __shfl_xor(k, off);
+          k = o > k ? o : k;
+        }
+        const int m = T::row(lane, q >> 2, q & 3);
+        if (T::out_lane(lane) && (lane % T::RED) == 0 && m < p.M && k != 0ull) {
+          const unsigned long long prev = __hip_atomic_fetch_max(&p.best[(w % kBuckets) * kMaxRows + m], k,
+                                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          asm volatile("" ::"v"(prev));  // keep the returning form: it completes before the wait below
+        }
+      }
+      wait_stores();
+      uint32_t old = 0;
+      if (lane == 0) old = __hip_atomic_fetch_add(p.done, (uint32_t)finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = __shfl(old, 0);
+      if (old + (uint32_t)finished == (uint32_t)p.tiles) head_final(p, lane);
+    }
+  }
 }
 
 // ------------------------------------------------------------------- probes
@@ -493,14 +680,20 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4_t* __restri
 // ---------------------------------------------------------------- launchers
 
 template <int FMT, int EPI>
-static int launch_mb(const GemmParams& p, hipStream_t st) {
-  const int mb = (p.M + 7) / 8;
+static int launch_rg(const GemmParams& p, hipStream_t st) {
+  const int rows = FMT == FMT_NVFP4 ? 8 : 16;
+  const int rg = (p.M + rows - 1) / rows;
   const dim3 grid((unsigned)((p.workers + 3) / 4)), block(256);
-  switch (mb) {
-    case 1: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p); break;
-    case 3: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 3>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 4>), grid, block, 0, st, p); break;
+  if constexpr (FMT == FMT_NVFP4) {
+    switch (rg) {
+      case 1: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p); break;
+      case 2: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p); break;
+      case 3: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 3>), grid, block, 0, st, p); break;
+      default: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 4>), grid, block, 0, st, p); break;
+    }
+  } else {
+    if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p);
   }
   return (int)hipGetLastError();
 }
@@ -508,11 +701,22 @@ static int launch_mb(const GemmParams& p, hipStream_t st) {
 int launch_gemm(int fmt, int epi, const GemmParams& p, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (fmt == FMT_NVFP4) {
-    if (epi == EPI_NONE) return launch_mb<FMT_NVFP4, EPI_NONE>(p, st);
-    if (epi == EPI_SILU) return launch_mb<FMT_NVFP4, EPI_SILU>(p, st);
-    return launch_mb<FMT_NVFP4, EPI_ARGMAX>(p, st);
+    if (epi == EPI_NONE) return launch_rg<FMT_NVFP4, EPI_NONE>(p, st);
+    if (epi == EPI_SILU) return launch_rg<FMT_NVFP4, EPI_SILU>(p, st);
+    return launch_rg<FMT_NVFP4, EPI_ARGMAX>(p, st);
   }
-  return launch_mb<FMT_FP8, EPI_NONE>(p, st);
+  return launch_rg<FMT_FP8, EPI_NONE>(p, st);
+}
+
+int launch_pack(int fmt, const PackParams& p, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t chunks = (int64_t)p.tiles * p.iters * (fmt == FMT_NVFP4 ? 288 : 512);
+  int64_t groups = (chunks + 255) / 256;
+  if (groups > 65536) groups = 65536;  // grid-stride beyond this
+  const dim3 grid((unsigned)groups), block(256);
+  if (fmt == FMT_NVFP4) hipLaunchKernelGGL(pack_nvfp4_kernel, grid, block, 0, st, p);
+  else hipLaunchKernelGGL(pack_fp8_kernel, grid, block, 0, st, p);
+  return (int)hipGetLastError();
 }
 
 int launch_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {

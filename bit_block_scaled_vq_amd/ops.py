@@ -31,8 +31,12 @@ VQ_OP_NVFP4 = 0
 VQ_OP_NVFP4_SILU_MUL = 1
 VQ_OP_FP8 = 2
 VQ_OP_LMHEAD = 3
+VQ_PACK_NVFP4 = 0
+VQ_PACK_NVFP4_GATE_UP = 1
+VQ_PACK_FP8 = 2
 
 EXPORTS = [
+    "vq_packed_bytes", "vq_pack_nvfp4", "vq_pack_fp8",
     "vq_gemm_nvfp4", "vq_gemm_fp8", "vq_lmhead_argmax_accept", "vq_workspace_bytes",
     "vq_status_str", "vq_last_error", "vq_abi_version", "vq_probe_copy", "vq_probe_read",
 ]
@@ -56,11 +60,17 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(f"libverify.so is not built ({LIB_PATH}); run `python -m bit_block_scaled_vq_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
-    L.vq_gemm_nvfp4.argtypes = [vp, vp, vp, f32, vp, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.vq_packed_bytes.argtypes = [i32, i32, i32]
+    L.vq_packed_bytes.restype = sz
+    L.vq_pack_nvfp4.argtypes = [vp, vp, i32, i32, i32, vp, sz, vp]
+    L.vq_pack_nvfp4.restype = i32
+    L.vq_pack_fp8.argtypes = [vp, i32, i32, vp, sz, vp]
+    L.vq_pack_fp8.restype = i32
+    L.vq_gemm_nvfp4.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, i32, i32, vp, sz, vp]
     L.vq_gemm_nvfp4.restype = i32
-    L.vq_gemm_fp8.argtypes = [vp, vp, f32, vp, i32, i32, i32, i32, vp, sz, vp]
+    L.vq_gemm_fp8.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, i32, vp, sz, vp]
     L.vq_gemm_fp8.restype = i32
-    L.vq_lmhead_argmax_accept.argtypes = [vp, vp, vp, f32, vp, i32, i32, i32, i32,
+    L.vq_lmhead_argmax_accept.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, i32,
                                           vp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.vq_lmhead_argmax_accept.restype = i32
     L.vq_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -139,50 +149,87 @@ def workspace(op: int, M: int, N: int, K: int, device="cuda"):
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def vq_gemm_nvfp4(x, codes, scales, tensor_scale: float, y, epilogue: int = VQ_EPI_NONE,
-                  workspace=None, stream=None):
-    """y[M][N] = x . W^T (NVFP4 W), or silu(gate)*up for VQ_EPI_SILU_MUL."""
+def packed_bytes(kind: int, rows: int, K: int) -> int:
+    return int(lib().vq_packed_bytes(kind, rows, K))
+
+
+def pack_nvfp4(codes, scales, gate_up: bool = False, stream=None):
+    """Packed form (1-D uint8 device tensor) of a canonical NVFP4 matrix
+    codes [rows][K/2], scales [rows][K/16]; gate_up packs a fused [gate; up]
+    matrix for VQ_EPI_SILU_MUL."""
     torch = _torch()
-    _need(x, "x", (torch.bfloat16,), 2)
     _need(codes, "codes", (torch.uint8,), 2)
     _need(scales, "scales", (torch.uint8,), 2)
+    rows, K = codes.shape[0], 2 * codes.shape[1]
+    if tuple(scales.shape) != (rows, K // 16):
+        raise ValueError(f"shape mismatch: codes {tuple(codes.shape)} scales {tuple(scales.shape)}")
+    n = packed_bytes(VQ_PACK_NVFP4_GATE_UP if gate_up else VQ_PACK_NVFP4, rows, K)
+    if n == 0:
+        raise VerifyError(VQ_ERR_SHAPE, f"invalid shape for packing: rows={rows} K={K}")
+    out = torch.empty(n, dtype=torch.uint8, device=codes.device)
+    _check(lib().vq_pack_nvfp4(_ptr(codes), _ptr(scales), rows, K, int(bool(gate_up)), _ptr(out), n,
+                               _stream(stream)))
+    return out
+
+
+def pack_fp8(w, stream=None):
+    """Packed form (1-D uint8 device tensor) of a canonical E4M3 matrix w [rows][K]."""
+    torch = _torch()
+    _need(w, "w", (torch.uint8,), 2)
+    rows, K = w.shape
+    n = packed_bytes(VQ_PACK_FP8, rows, K)
+    if n == 0:
+        raise VerifyError(VQ_ERR_SHAPE, f"invalid shape for packing: rows={rows} K={K}")
+    out = torch.empty(n, dtype=torch.uint8, device=w.device)
+    _check(lib().vq_pack_fp8(_ptr(w), rows, K, _ptr(out), n, _stream(stream)))
+    return out
+
+
+def _ws(workspace):
+    return (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+
+
+def vq_gemm_nvfp4(x, w, tensor_scale: float, y, epilogue: int = VQ_EPI_NONE, workspace=None, stream=None):
+    """y[M][N] = x . W^T (NVFP4 W, packed by pack_nvfp4), or silu(gate)*up for
+    VQ_EPI_SILU_MUL (w packed with gate_up=True)."""
+    torch = _torch()
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(w, "w", (torch.uint8,), 1)
     _need(y, "y", (torch.bfloat16, torch.float32), 2)
     M, K = x.shape
     N = y.shape[1]
-    nw = 2 * N if epilogue == VQ_EPI_SILU_MUL else N
-    if y.shape[0] != M or tuple(codes.shape) != (nw, K // 2) or tuple(scales.shape) != (nw, K // 16):
-        raise ValueError(f"shape mismatch: x {tuple(x.shape)} codes {tuple(codes.shape)} "
-                         f"scales {tuple(scales.shape)} y {tuple(y.shape)}")
-    ws_ptr, ws_n = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
-    _check(lib().vq_gemm_nvfp4(_ptr(x), _ptr(codes), _ptr(scales), float(tensor_scale), _ptr(y),
+    if y.shape[0] != M:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)} y {tuple(y.shape)}")
+    ws_ptr, ws_n = _ws(workspace)
+    _check(lib().vq_gemm_nvfp4(_ptr(x), _ptr(w), w.numel(), float(tensor_scale), _ptr(y),
                                _out_dtype(y), M, N, K, int(epilogue), ws_ptr, ws_n, _stream(stream)))
     return y
 
 
 def vq_gemm_fp8(x, w, w_scale: float, y, workspace=None, stream=None):
-    """y[M][N] = (x . E4M3(w)^T) * w_scale."""
+    """y[M][N] = (x . E4M3(W)^T) * w_scale, W packed by pack_fp8."""
     torch = _torch()
     _need(x, "x", (torch.bfloat16,), 2)
-    _need(w, "w", (torch.uint8,), 2)
+    _need(w, "w", (torch.uint8,), 1)
     _need(y, "y", (torch.bfloat16, torch.float32), 2)
     M, K = x.shape
-    N = w.shape[0]
-    if tuple(y.shape) != (M, N) or w.shape[1] != K:
-        raise ValueError(f"shape mismatch: x {tuple(x.shape)} w {tuple(w.shape)} y {tuple(y.shape)}")
-    ws_ptr, ws_n = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
-    _check(lib().vq_gemm_fp8(_ptr(x), _ptr(w), float(w_scale), _ptr(y), _out_dtype(y), M, N, K,
+    N = y.shape[1]
+    if y.shape[0] != M:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)} y {tuple(y.shape)}")
+    ws_ptr, ws_n = _ws(workspace)
+    _check(lib().vq_gemm_fp8(_ptr(x), _ptr(w), w.numel(), float(w_scale), _ptr(y), _out_dtype(y), M, N, K,
                              ws_ptr, ws_n, _stream(stream)))
     return y
 
 
-def vq_lmhead_argmax_accept(h, codes, scales, tensor_scale: float, draft, lanes: int, R: int,
+def vq_lmhead_argmax_accept(h, w, tensor_scale: float, V: int, draft, lanes: int, R: int,
                             argmax_out, accept_len_out, maxlogit_out=None, commit_out=None,
                             logits_out=None, workspace=None, stream=None):
-    """Vocabulary head + per-row argmax + greedy accept (results stay on the device)."""
+    """Vocabulary head (W [V][K] packed by pack_nvfp4) + per-row argmax + greedy
+    accept; results stay on the device."""
     torch = _torch()
     _need(h, "h", (torch.bfloat16,), 2)
-    _need(codes, "codes", (torch.uint8,), 2)
-    _need(scales, "scales", (torch.uint8,), 2)
+    _need(w, "w", (torch.uint8,), 1)
     _need(argmax_out, "argmax_out", (torch.int32,), 1)
     _need(accept_len_out, "accept_len_out", (torch.int32,), 1)
     if draft is not None:
@@ -194,9 +241,8 @@ def vq_lmhead_argmax_accept(h, codes, scales, tensor_scale: float, draft, lanes:
     if logits_out is not None:
         _need(logits_out, "logits_out", (torch.bfloat16, torch.float32), 2)
     M, K = h.shape
-    V = codes.shape[0]
-    if M != lanes * R or tuple(codes.shape) != (V, K // 2) or tuple(scales.shape) != (V, K // 16):
-        raise ValueError("shape mismatch between h, lanes*R and the head")
+    if M != lanes * R:
+        raise ValueError("h must have lanes * R rows")
     if argmax_out.numel() != M or accept_len_out.numel() != lanes:
         raise ValueError("output sizes do not match lanes and R")
     if draft is not None and tuple(draft.shape) != (lanes, R - 1):
@@ -205,10 +251,10 @@ def vq_lmhead_argmax_accept(h, codes, scales, tensor_scale: float, draft, lanes:
         raise ValueError("commit_out must be [lanes][R]")
     if logits_out is not None and tuple(logits_out.shape) != (M, V):
         raise ValueError("logits_out must be [M][V]")
-    ws_ptr, ws_n = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    ws_ptr, ws_n = _ws(workspace)
     ld = _out_dtype(logits_out) if logits_out is not None else VQ_OUT_F32
     _check(lib().vq_lmhead_argmax_accept(
-        _ptr(h), _ptr(codes), _ptr(scales), float(tensor_scale), _ptr(draft), lanes, R, V, K,
+        _ptr(h), _ptr(w), w.numel(), float(tensor_scale), _ptr(draft), lanes, R, V, K,
         _ptr(argmax_out), _ptr(maxlogit_out), _ptr(accept_len_out), _ptr(commit_out),
         _ptr(logits_out), ld, ws_ptr, ws_n, _stream(stream)))
 

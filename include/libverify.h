@@ -17,6 +17,29 @@
  * The pass ends in the vocabulary head, a per-row argmax and the greedy accept
  * length ("lithos-metal ...", section "How DSpark is wired in").
  *
+ * Weights are consumed in a packed layout that the library builds once from
+ * the canonical layout (vq_pack_nvfp4 / vq_pack_fp8, at weight-load time; the
+ * lithos-metal page, section "The control experiment the blog leaves out",
+ * credits a weight layout packed for the memory bus).
+ * Canonical layout: NVFP4 codes uint8 [rows][K/2], byte j of a row holds
+ * element k = 2j in its low nibble and k = 2j+1 in its high nibble; scales
+ * uint8 [rows][K/16] (E4M3FN: no infinities, NaN = S.1111.111, max 448), scale
+ * byte b covers k in [16b, 16b+16). FP8 weights uint8 [rows][K] (E4M3FN).
+ * Packed layout (bytes are moved, never changed): rows are cut into tiles of
+ * 64 (four sub-tiles of 16 rows; for a fused SwiGLU [gate; up] matrix a tile
+ * holds 32 gate rows and the 32 up rows of the same output columns), K into
+ * iterations of 128, and each (tile, iteration) is one contiguous block, tiles
+ * in order and iterations in order inside a tile.
+ *   NVFP4 block, 4608 B: for sub-tile t and lane l = 16g + n, the 16 bytes at
+ *   1024t + 16l are the code bytes of k 32j + 8g .. 32j + 8g + 7 (j = 0..3) of
+ *   the sub-tile's row n; then for half h and row n, the 16 bytes at
+ *   4096 + 16(16h + n) hold for each sub-tile t (4 bytes) the scales of blocks
+ *   2j + h, j = 0..3 (block index inside the iteration).
+ *   FP8 block, 8192 B: for sub-tile t, half h and lane l = 16g + n, the 16
+ *   bytes at 1024(2t + h) + 16l are the weights of k 64h + 8g .. +7 and
+ *   64h + 32 + 8g .. +7 of row n.
+ * Rows past the matrix are zero. Sizes come from vq_packed_bytes().
+ *
  * Conventions shared by every entry point
  *   - All data pointers are DEVICE pointers owned by the caller; arrays are
  *     dense and row-major. The library never allocates, frees, synchronises or
@@ -24,16 +47,13 @@
  *     (a hipStream_t; NULL is the default stream) and can be captured into a
  *     HIP graph.
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
- *   - NVFP4 layout: codes uint8 [rows][K/2], byte j of a row holds element
- *     k = 2j in its low nibble and k = 2j+1 in its high nibble; scales uint8
- *     [rows][K/16] (E4M3FN: no infinities, NaN = S.1111.111, max 448), scale
- *     byte b covers k in [16b, 16b+16).
  *   - Every argument is validated on the host before any HIP call; on error
  *     nothing is launched and a non-zero vq_status is returned, with detail in
- *     vq_last_error(). Shapes: 1 <= M <= 32, N >= 1, K >= 64 and K % 64 == 0.
- *     x, h, codes, scales and w must be 16-byte aligned (every row then is);
- *     y and logits must be aligned to their element size; int32/f32 arrays
- *     4-byte aligned; the workspace 16-byte aligned.
+ *     vq_last_error(). Shapes: 1 <= M <= 32, N >= 1, K >= 128 and K % 128 == 0.
+ *     x, h, canonical and packed weights must be 16-byte aligned (every row
+ *     then is); y and logits must be aligned to their element size; int32/f32
+ *     arrays 4-byte aligned; the workspace 16-byte aligned. A packed size
+ *     (w_bytes) smaller than the shape needs returns VQ_ERR_SHAPE.
  *   - workspace: device memory of at least vq_workspace_bytes(op, M, N, K)
  *     bytes, zero-filled by the caller ONCE before its first use. Kernels leave
  *     every counter in it at zero again, so one workspace can be reused by
@@ -41,8 +61,8 @@
  *     may run concurrently need distinct workspaces. A NULL or short workspace
  *     returns VQ_ERR_WORKSPACE; the schedule never changes silently.
  *   - Results are deterministic: the K partition and the order of the fixed
- *     split-K reduction depend only on (N, K) and the epilogue, never
- *     on M, so row r of an M-row call equals row r of any other M.
+ *     split-K reduction depend only on (N, K) and the epilogue, never on M,
+ *     so row r of an M-row call equals row r of any other M bit for bit.
  *   - The first call on a device checks that it is gfx950 (VQ_ERR_DEVICE).
  *     A failed launch returns VQ_ERR_LAUNCH.
  *   - Thread-safe; vq_last_error() is per host thread.
@@ -57,12 +77,12 @@
 extern "C" {
 #endif
 
-#define VQ_ABI_VERSION 1
+#define VQ_ABI_VERSION 2
 
 typedef enum {
   VQ_OK = 0,
   VQ_ERR_NULL = 1,      /* a required pointer is NULL */
-  VQ_ERR_SHAPE = 2,     /* M, N, K, lanes, R or V out of range */
+  VQ_ERR_SHAPE = 2,     /* M, N, K, lanes, R, V or a size out of range */
   VQ_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
   VQ_ERR_WORKSPACE = 4, /* workspace NULL or smaller than vq_workspace_bytes() */
   VQ_ERR_DEVICE = 5,    /* no HIP device, or the current device is not gfx950 */
@@ -73,22 +93,41 @@ typedef enum {
 typedef enum { VQ_OUT_BF16 = 0, VQ_OUT_F32 = 1 } vq_out_dtype;
 typedef enum { VQ_EPI_NONE = 0, VQ_EPI_SILU_MUL = 1 } vq_epilogue;
 typedef enum { VQ_OP_NVFP4 = 0, VQ_OP_NVFP4_SILU_MUL = 1, VQ_OP_FP8 = 2, VQ_OP_LMHEAD = 3 } vq_op;
+typedef enum { VQ_PACK_NVFP4 = 0, VQ_PACK_NVFP4_GATE_UP = 1, VQ_PACK_FP8 = 2 } vq_pack_kind;
+
+/* Bytes of the packed form of a canonical matrix of `rows` rows and K columns
+ * (VQ_PACK_NVFP4_GATE_UP: the fused [gate; up] matrix, rows = 2N, even).
+ * Returns 0 for an invalid kind or shape. */
+size_t vq_packed_bytes(int32_t kind, int32_t rows, int32_t K);
+
+/* Pack a canonical NVFP4 matrix (codes [rows][K/2], scales [rows][K/16]) into
+ * `packed` (at least vq_packed_bytes() bytes). gate_up = 1 packs a fused
+ * SwiGLU [gate; up] matrix (rows = 2N) for VQ_EPI_SILU_MUL; 0 packs plain rows
+ * (VQ_EPI_NONE and the vocabulary head). A one-time, bandwidth-bound copy on
+ * `stream`; `packed` must not overlap the inputs. Returns a vq_status. */
+int32_t vq_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, int32_t rows, int32_t K,
+                      int32_t gate_up, uint8_t* packed, size_t packed_bytes, void* stream);
+
+/* Pack a canonical FP8 E4M3 matrix w [rows][K] into `packed`. */
+int32_t vq_pack_fp8(const uint8_t* w, int32_t rows, int32_t K, uint8_t* packed, size_t packed_bytes,
+                    void* stream);
 
 /* NVFP4 skinny GEMM: Y[M][N] = X[M][K] . W^T with
  *   W[n][k] = E2M1(code[n][k]) * E4M3(scale[n][k/16]) * tensor_scale
  * (formats: "lithos-metal ...", sections "What one token costs the bus" and
  * "Formats, and what runs where"; 9 bytes per 16 weights).
  *   x       bf16 [M][K]
- *   codes   uint8 [Nw][K/2], scales uint8 [Nw][K/16]
- *   epilogue VQ_EPI_NONE:     Nw = N, Y = X . W^T
- *            VQ_EPI_SILU_MUL: Nw = 2N, rows [0,N) are the SwiGLU gate and rows
+ *   w       packed weights, w_bytes bytes
+ *   epilogue VQ_EPI_NONE:     w = vq_pack_nvfp4(gate_up = 0) of W [N][K]
+ *            VQ_EPI_SILU_MUL: w = vq_pack_nvfp4(gate_up = 1) of the fused
+ *            [2N][K] matrix whose rows [0,N) are the SwiGLU gate and rows
  *            [N,2N) the up projection; Y = silu(gate) * up with silu(g) =
  *            g / (1 + exp(-g)), computed in fp32 before the single rounding of
  *            the store ("144 tok/s ...", section "The engine hard-codes the
  *            model": SwiGLU gate, up, down).
  *   y       [M][N], bf16 (round to nearest even) or fp32 per y_dtype.
  * Returns a vq_status. */
-int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
+int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* w, size_t w_bytes,
                       float tensor_scale, void* y, int32_t y_dtype,
                       int32_t M, int32_t N, int32_t K, int32_t epilogue,
                       void* workspace, size_t workspace_bytes, void* stream);
@@ -96,8 +135,9 @@ int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* codes, const uint8_t* sc
 /* FP8 skinny GEMM: Y[M][N] = (X[M][K] . E4M3(w)^T) * w_scale
  * ("lithos-metal ...", section "What one token costs the bus": every Gated
  * DeltaNet and attention projection is FP8 with a scalar scale).
- *   x bf16 [M][K]; w uint8 [N][K] (E4M3FN codes); y [M][N] bf16 or fp32. */
-int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, float w_scale,
+ *   x bf16 [M][K]; w = vq_pack_fp8 of the E4M3FN codes [N][K] (w_bytes
+ *   bytes); y [M][N] bf16 or fp32. */
+int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, size_t w_bytes, float w_scale,
                     void* y, int32_t y_dtype, int32_t M, int32_t N, int32_t K,
                     void* workspace, size_t workspace_bytes, void* stream);
 
@@ -107,7 +147,8 @@ int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, float w_scale,
  * "lithos-metal ...", section "How DSpark is wired in": the accept scan).
  *   h       bf16 [M][K] hidden rows, M = lanes * R; rows l*R .. l*R+R-1
  *           belong to lane l (row 0 of a lane follows its anchor token)
- *   codes, scales, tensor_scale: the NVFP4 head W_head [V][K] (layout above)
+ *   w, w_bytes, tensor_scale: the NVFP4 head W_head [V][K], packed with
+ *           vq_pack_nvfp4(gate_up = 0)
  *   draft   int32 [lanes][R-1]: draft j of lane l is compared with the argmax
  *           of row l*R + j. Ids are not validated; an id outside [0,V) never
  *           matches, and a row whose argmax is -1 matches no draft.
@@ -120,7 +161,7 @@ int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, float w_scale,
  *                  rows 0..accept_len-1 of the lane), -1 after them
  *   logits_out     [M][V] bf16 or fp32 per logits_dtype, or NULL
  * Shapes: 1 <= lanes <= 4, 1 <= R <= 8, 1 <= V <= 2^30, K as above. */
-int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* codes, const uint8_t* scales,
+int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* w, size_t w_bytes,
                                 float tensor_scale, const int32_t* draft,
                                 int32_t lanes, int32_t R, int32_t V, int32_t K,
                                 int32_t* argmax_out, float* maxlogit_out,

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = ops.lib()
-    assert L.vq_abi_version() == 1
+    assert L.vq_abi_version() == 2
     assert ops.status_str(ops.VQ_OK) == "VQ_OK"
     assert ops.status_str(ops.VQ_ERR_WORKSPACE) == "VQ_ERR_WORKSPACE"
     assert ops.status_str(99) == "VQ_ERR_UNKNOWN"
@@ -42,8 +42,8 @@ def test_version_and_status_strings():
 A = 1 << 20  # a fake, 16-byte-aligned address: never dereferenced (validation fails first)
 
 
-def _nvfp4(x=A, c=A, s=A, y=A, yd=0, M=8, N=1024, K=512, epi=0, ws=A, wsn=1 << 30):
-    return ops.lib().vq_gemm_nvfp4(x, c, s, 1.0, y, yd, M, N, K, epi, ws, wsn, None)
+def _nvfp4(x=A, w=A, wn=1 << 30, y=A, yd=0, M=8, N=1024, K=512, epi=0, ws=A, wsn=1 << 30):
+    return ops.lib().vq_gemm_nvfp4(x, w, wn, 1.0, y, yd, M, N, K, epi, ws, wsn, None)
 
 
 def test_gemm_nvfp4_validation():
@@ -54,10 +54,16 @@ def test_gemm_nvfp4_validation():
     assert _nvfp4(N=0) == ops.VQ_ERR_SHAPE
     assert _nvfp4(K=32) == ops.VQ_ERR_SHAPE
     assert _nvfp4(K=96) == ops.VQ_ERR_SHAPE
+    assert _nvfp4(K=192) == ops.VQ_ERR_SHAPE
     assert _nvfp4(yd=5) == ops.VQ_ERR_VALUE
     assert _nvfp4(epi=3) == ops.VQ_ERR_VALUE
     assert _nvfp4(x=A + 8) == ops.VQ_ERR_ALIGN
-    assert _nvfp4(c=A + 4) == ops.VQ_ERR_ALIGN
+    assert _nvfp4(w=None) == ops.VQ_ERR_NULL
+    assert _nvfp4(w=A + 4) == ops.VQ_ERR_ALIGN
+    need = ops.packed_bytes(ops.VQ_PACK_NVFP4, 1024, 512)
+    assert _nvfp4(wn=need - 1) == ops.VQ_ERR_SHAPE
+    need_gu = ops.packed_bytes(ops.VQ_PACK_NVFP4_GATE_UP, 2048, 512)
+    assert _nvfp4(epi=1, wn=need_gu - 16) == ops.VQ_ERR_SHAPE
     assert _nvfp4(y=A + 1) == ops.VQ_ERR_ALIGN
     assert _nvfp4(ws=None) == ops.VQ_ERR_WORKSPACE
     assert _nvfp4(wsn=16) == ops.VQ_ERR_WORKSPACE
@@ -66,14 +72,17 @@ def test_gemm_nvfp4_validation():
 
 def test_gemm_fp8_validation():
     L = ops.lib()
-    assert L.vq_gemm_fp8(None, A, 1.0, A, 0, 8, 64, 64, A, 1 << 30, None) == ops.VQ_ERR_NULL
-    assert L.vq_gemm_fp8(A, A, 1.0, A, 0, 8, 64, 100, A, 1 << 30, None) == ops.VQ_ERR_SHAPE
-    assert L.vq_gemm_fp8(A, A + 2, 1.0, A, 0, 8, 64, 64, A, 1 << 30, None) == ops.VQ_ERR_ALIGN
-    assert L.vq_gemm_fp8(A, A, 1.0, A, 0, 8, 64, 64, A, 0, None) == ops.VQ_ERR_WORKSPACE
+    big = 1 << 30
+    assert L.vq_gemm_fp8(None, A, big, 1.0, A, 0, 8, 64, 128, A, big, None) == ops.VQ_ERR_NULL
+    assert L.vq_gemm_fp8(A, A, big, 1.0, A, 0, 8, 64, 100, A, big, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_gemm_fp8(A, A, big, 1.0, A, 0, 8, 64, 64, A, big, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_gemm_fp8(A, A + 2, big, 1.0, A, 0, 8, 64, 128, A, big, None) == ops.VQ_ERR_ALIGN
+    assert L.vq_gemm_fp8(A, A, 8191, 1.0, A, 0, 8, 64, 128, A, big, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_gemm_fp8(A, A, big, 1.0, A, 0, 8, 64, 128, A, 0, None) == ops.VQ_ERR_WORKSPACE
 
 
 def _head(h=A, draft=A, lanes=1, R=8, V=1000, K=256, am=A, al=A, logits=None, ld=1, ws=A, wsn=1 << 30):
-    return ops.lib().vq_lmhead_argmax_accept(h, A, A, 1.0, draft, lanes, R, V, K, am, None, al, None,
+    return ops.lib().vq_lmhead_argmax_accept(h, A, 1 << 30, 1.0, draft, lanes, R, V, K, am, None, al, None,
                                              logits, ld, ws, wsn, None)
 
 
@@ -92,13 +101,47 @@ def test_lmhead_validation():
 
 def test_workspace_bytes():
     L = ops.lib()
-    assert L.vq_workspace_bytes(ops.VQ_OP_NVFP4, 0, 10, 64) == 0
-    assert L.vq_workspace_bytes(ops.VQ_OP_NVFP4, 8, 10, 60) == 0
+    assert L.vq_workspace_bytes(ops.VQ_OP_NVFP4, 0, 10, 128) == 0
+    assert L.vq_workspace_bytes(ops.VQ_OP_NVFP4, 8, 10, 64) == 0
+    assert L.vq_workspace_bytes(ops.VQ_OP_NVFP4, 8, 10, 128) > 0
     assert L.vq_workspace_bytes(9, 8, 10, 64) == 0
     for op in (ops.VQ_OP_NVFP4, ops.VQ_OP_NVFP4_SILU_MUL, ops.VQ_OP_FP8, ops.VQ_OP_LMHEAD):
         sizes = {L.vq_workspace_bytes(op, m, 17408, 5120) for m in (1, 8, 16, 24, 32)}
         assert len(sizes) == 1 and sizes.pop() > 0          # M-independent
     assert L.vq_workspace_bytes(ops.VQ_OP_LMHEAD, 8, 248320, 5120) > L.vq_workspace_bytes(ops.VQ_OP_NVFP4, 8, 248320, 5120)
+
+
+def test_packed_bytes():
+    L = ops.lib()
+    # 64-row tiles x 128-K iterations; NVFP4 blocks 4096 B of codes + 512 B of
+    # scales (9 bytes per 16 weights), FP8 blocks 8192 B (one byte per weight)
+    assert L.vq_packed_bytes(ops.VQ_PACK_NVFP4, 64, 128) == 4608 == 64 * 128 * 9 // 16
+    assert L.vq_packed_bytes(ops.VQ_PACK_NVFP4, 65, 256) == 2 * 2 * 4608
+    assert L.vq_packed_bytes(ops.VQ_PACK_NVFP4_GATE_UP, 64, 128) == 4608
+    assert L.vq_packed_bytes(ops.VQ_PACK_NVFP4_GATE_UP, 66, 128) == 2 * 4608
+    assert L.vq_packed_bytes(ops.VQ_PACK_NVFP4_GATE_UP, 63, 128) == 0
+    assert L.vq_packed_bytes(ops.VQ_PACK_FP8, 130, 384) == 3 * 3 * 8192
+    assert L.vq_packed_bytes(ops.VQ_PACK_FP8, 0, 128) == 0
+    assert L.vq_packed_bytes(ops.VQ_PACK_FP8, 64, 100) == 0
+    assert L.vq_packed_bytes(7, 64, 128) == 0
+    # the model's matrices pack without padding (row counts are multiples of 64)
+    assert L.vq_packed_bytes(ops.VQ_PACK_NVFP4_GATE_UP, 2 * 17408, 5120) == 2 * 17408 * 5120 * 9 // 16
+    assert L.vq_packed_bytes(ops.VQ_PACK_NVFP4, 248320, 5120) == 248320 * 5120 * 9 // 16
+
+
+def test_pack_validation():
+    L = ops.lib()
+    n = 1 << 30
+    assert L.vq_pack_nvfp4(None, A, 64, 128, 0, A, n, None) == ops.VQ_ERR_NULL
+    assert L.vq_pack_nvfp4(A, A, 64, 128, 2, A, n, None) == ops.VQ_ERR_VALUE
+    assert L.vq_pack_nvfp4(A, A, 63, 128, 1, A, n, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_pack_nvfp4(A, A, 64, 96, 0, A, n, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_pack_nvfp4(A, A + 1, 64, 128, 0, A, n, None) == ops.VQ_ERR_ALIGN
+    assert L.vq_pack_nvfp4(A, A, 64, 128, 0, A, 4607, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_pack_fp8(A, 64, 128, None, n, None) == ops.VQ_ERR_NULL
+    assert L.vq_pack_fp8(A, 0, 128, A, n, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_pack_fp8(A, 64, 128, A + 8, n, None) == ops.VQ_ERR_ALIGN
+    assert L.vq_pack_fp8(A, 64, 128, A, 8191, None) == ops.VQ_ERR_SHAPE
 
 
 def _gpu_visible():
@@ -112,6 +155,7 @@ def _gpu_visible():
 @pytest.mark.skipif(_gpu_visible(), reason="would pass validation and launch with fake pointers")
 def test_valid_call_without_gpu_reports_device_error():
     assert _nvfp4() == ops.VQ_ERR_DEVICE
+    assert ops.lib().vq_pack_fp8(A, 64, 128, A, 1 << 30, None) == ops.VQ_ERR_DEVICE
     assert ops.lib().vq_probe_copy(A, A, 1024, None) == ops.VQ_ERR_DEVICE
 
 

@@ -11,8 +11,8 @@ import pytest
 
 import oracle as O
 from bit_block_scaled_vq_amd import inputs
-from tests.gpu_helpers import (bf16_to_bits, check_bf16_store, check_f32, say, to_dev_bf16, to_dev_u8,
-                               torch_dev)
+from tests.gpu_helpers import (bf16_to_bits, check_bf16_store, check_f32, pack_fp8_np, pack_nvfp4_np, say,
+                               to_dev_bf16, to_dev_u8, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,17 +26,16 @@ def run_nvfp4(x_bits, codes, scales, ts, n_out, epi=0, out="both", ws=None):
     torch, dev = torch_dev()
     ops = _ops()
     x = to_dev_bf16(x_bits)
-    c = to_dev_u8(codes)
-    s = to_dev_u8(scales)
+    w = ops.pack_nvfp4(to_dev_u8(codes), to_dev_u8(scales), gate_up=bool(epi))
     m, k = x_bits.shape
     op = ops.VQ_OP_NVFP4_SILU_MUL if epi else ops.VQ_OP_NVFP4
     ws = ws if ws is not None else ops.workspace(op, m, n_out, k, dev)
     y32 = torch.empty((m, n_out), dtype=torch.float32, device=dev)
-    ops.vq_gemm_nvfp4(x, c, s, ts, y32, epilogue=epi, workspace=ws)
+    ops.vq_gemm_nvfp4(x, w, ts, y32, epilogue=epi, workspace=ws)
     res = {"f32": y32.cpu().numpy()}
     if out == "both":
         yb = torch.empty((m, n_out), dtype=torch.bfloat16, device=dev)
-        ops.vq_gemm_nvfp4(x, c, s, ts, yb, epilogue=epi, workspace=ws)
+        ops.vq_gemm_nvfp4(x, w, ts, yb, epilogue=epi, workspace=ws)
         res["bf16"] = bf16_to_bits(yb)
     torch.cuda.synchronize()
     return res
@@ -46,7 +45,7 @@ def run_fp8(x_bits, w, wscale, out="both"):
     torch, dev = torch_dev()
     ops = _ops()
     x = to_dev_bf16(x_bits)
-    wd = to_dev_u8(w)
+    wd = ops.pack_fp8(to_dev_u8(w))
     m, k = x_bits.shape
     n = w.shape[0]
     ws = ops.workspace(ops.VQ_OP_FP8, m, n, k, dev)
@@ -59,6 +58,31 @@ def run_fp8(x_bits, w, wscale, out="both"):
         res["bf16"] = bf16_to_bits(yb)
     torch.cuda.synchronize()
     return res
+
+
+# ------------------------------------------------------------- packing
+
+@pytest.mark.parametrize("rows,k,gate_up", [(100, 384, False), (64, 128, False), (140, 256, True),
+                                           (2, 128, True), (1, 512, False)])
+def test_pack_nvfp4_layout(rows, k, gate_up):
+    say(f"case: pack NVFP4 rows={rows} K={k} gate_up={gate_up}")
+    ops = _ops()
+    codes, scales = inputs.nvfp4_weights((300, rows, k), rows, k)
+    got = ops.pack_nvfp4(to_dev_u8(codes), to_dev_u8(scales), gate_up=gate_up).cpu().numpy()
+    want = pack_nvfp4_np(codes, scales, gate_up)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("rows,k", [(130, 512), (64, 128), (1, 256)])
+def test_pack_fp8_layout(rows, k):
+    say(f"case: pack FP8 rows={rows} K={k}")
+    ops = _ops()
+    w = np.random.default_rng(rows).integers(0, 256, size=(rows, k), dtype=np.uint8)
+    got = ops.pack_fp8(to_dev_u8(w)).cpu().numpy()
+    want = pack_fp8_np(w)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
 
 
 # ------------------------------------------------------------------- NVFP4
@@ -74,9 +98,9 @@ def test_nvfp4_single_gemm_m8_k512_n1024():
 
 
 @pytest.mark.parametrize("m,n,k,ts", [
-    (1, 1, 64, 1.0), (3, 33, 192, 0.37), (8, 100, 512, 1.0), (13, 257, 320, 2.5),
+    (1, 1, 128, 1.0), (3, 33, 384, 0.37), (8, 100, 512, 1.0), (13, 257, 640, 2.5),
     (24, 64, 1024, 1.0), (32, 200, 256, 0.125), (8, 4096, 2048, 1.0), (5, 1000, 5120, 1.0),
-    (16, 2, 128, 1.0), (8, 65, 64, 1.0),
+    (16, 2, 128, 1.0), (8, 65, 128, 1.0), (9, 130, 768, 1.0), (7, 3000, 17408, 1.0),
 ])
 def test_nvfp4_shapes(m, n, k, ts):
     say(f"case: NVFP4 M={m} N={n} K={k} ts={ts}")
@@ -91,10 +115,10 @@ def test_nvfp4_shapes(m, n, k, ts):
 def test_nvfp4_one_hot_is_bit_exact():
     # Y[0, n] = W[n, k] * 1.0 exactly: pins the decode, the nibble order, the
     # scale-block mapping and the operand roles.
-    n, k, ts = 130, 320, 0.75
+    n, k, ts = 130, 384, 0.75
     codes, scales = inputs.nvfp4_weights((101,), n, k)
     w = O.dequant_nvfp4(codes, scales, ts)
-    for kk in (0, 1, 7, 8, 15, 16, 31, 32, 63, 64, 100, 255, 256, 319):
+    for kk in (0, 1, 7, 8, 15, 16, 31, 32, 63, 64, 100, 127, 128, 255, 256, 383):
         say(f"case: one-hot k={kk}")
         x = np.zeros((1, k), dtype=np.uint16)
         x[0, kk] = 0x3F80
@@ -155,7 +179,8 @@ def test_mlp_layer_m8_full_size():
 # --------------------------------------------------------------------- FP8
 
 @pytest.mark.parametrize("m,n,k,ws", [
-    (1, 1, 64, 1.0), (8, 100, 512, 0.37), (13, 257, 320, 0.125), (32, 64, 1024, 1.0), (8, 1000, 6144, 1.0),
+    (1, 1, 128, 1.0), (8, 100, 512, 0.37), (13, 257, 640, 0.125), (32, 64, 1024, 1.0), (8, 1000, 6144, 1.0),
+    (24, 3000, 5120, 1.0),
 ])
 def test_fp8_shapes(m, n, k, ws):
     say(f"case: FP8 M={m} N={n} K={k} scale={ws}")
@@ -169,7 +194,7 @@ def test_fp8_shapes(m, n, k, ws):
 
 def test_fp8_all_codes_one_hot():
     # every E4M3 code (NaN codes included) decoded exactly by the kernel
-    n, k = 256, 64
+    n, k = 256, 128
     w = np.zeros((n, k), dtype=np.uint8)
     w[:, 5] = np.arange(256, dtype=np.uint8)
     x = np.zeros((1, k), dtype=np.uint16)
@@ -184,25 +209,45 @@ def test_fp8_all_codes_one_hot():
 # ---------------------------------------------- properties of the schedule
 
 def test_rows_independent_of_m_and_deterministic():
+    # the K partition and the reduction order depend only on (N, K): the rows
+    # shared by calls with different M are bitwise equal.
     torch, dev = torch_dev()
     ops = _ops()
     n, k = 5120, 17408        # the narrow, long-K down projection shape
     codes, scales = inputs.nvfp4_weights((105,), n, k)
     x32 = inputs.x_bf16((105,), 32, k)
-    c, s = to_dev_u8(codes), to_dev_u8(scales)
+    w = ops.pack_nvfp4(to_dev_u8(codes), to_dev_u8(scales))
     ws = ops.workspace(ops.VQ_OP_NVFP4, 32, n, k, dev)
     outs = {}
-    for m in (32, 8, 1, 24, 16):
+    for m in (32, 8, 1, 24, 16, 5, 9):
+        say(f"case: down projection M={m}")
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
-        ops.vq_gemm_nvfp4(to_dev_bf16(x32[:m]), c, s, 1.0, y, workspace=ws)
+        ops.vq_gemm_nvfp4(to_dev_bf16(x32[:m]), w, 1.0, y, workspace=ws)
         outs[m] = y.cpu().numpy()
-    for m in (8, 1, 24, 16):
+    for m in (1, 5, 8, 9, 16, 24):
         assert np.array_equal(outs[m], outs[32][:m]), m
     y2 = torch.empty((32, n), dtype=torch.float32, device=dev)
-    ops.vq_gemm_nvfp4(to_dev_bf16(x32), c, s, 1.0, y2, workspace=ws)
+    ops.vq_gemm_nvfp4(to_dev_bf16(x32), w, 1.0, y2, workspace=ws)
     assert np.array_equal(y2.cpu().numpy(), outs[32])
-    ref = O.gemm_nvfp4(x32[:8], codes, scales, 1.0)
-    check_f32(outs[8], ref, what="down M=8")
+    ref = O.gemm_nvfp4(x32, codes, scales, 1.0)
+    check_f32(outs[8], ref[:8], what="down M=8")
+    check_f32(outs[32], ref, what="down M=32")
+
+
+def test_fp8_rows_independent_of_m():
+    torch, dev = torch_dev()
+    ops = _ops()
+    n, k = 1000, 6144
+    w = ops.pack_fp8(to_dev_u8(inputs.fp8_weights((107,), n, k)))
+    x32 = inputs.x_bf16((107,), 32, k)
+    ws = ops.workspace(ops.VQ_OP_FP8, 32, n, k, dev)
+    outs = {}
+    for m in (32, 8, 17):
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        ops.vq_gemm_fp8(to_dev_bf16(x32[:m]), w, 0.5, y, workspace=ws)
+        outs[m] = y.cpu().numpy()
+    for m in (8, 17):
+        assert np.array_equal(outs[m], outs[32][:m]), m
 
 
 def test_graph_capture_and_replay():
@@ -211,10 +256,11 @@ def test_graph_capture_and_replay():
     m, n, k = 8, 2048, 1024
     x = inputs.x_bf16((106,), m, k)
     codes, scales = inputs.nvfp4_weights((106,), n, k)
-    xd, c, s = to_dev_bf16(x), to_dev_u8(codes), to_dev_u8(scales)
+    xd = to_dev_bf16(x)
+    w = ops.pack_nvfp4(to_dev_u8(codes), to_dev_u8(scales))
     ws = ops.workspace(ops.VQ_OP_NVFP4, m, n, k, dev)
     y_eager = torch.empty((m, n), dtype=torch.float32, device=dev)
-    ops.vq_gemm_nvfp4(xd, c, s, 1.0, y_eager, workspace=ws)
+    ops.vq_gemm_nvfp4(xd, w, 1.0, y_eager, workspace=ws)
     eager = y_eager.cpu().numpy()
     y = torch.zeros((m, n), dtype=torch.float32, device=dev)
     g = torch.cuda.CUDAGraph()
@@ -222,7 +268,7 @@ def test_graph_capture_and_replay():
     st.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(st):
         with torch.cuda.graph(g, stream=st):
-            ops.vq_gemm_nvfp4(xd, c, s, 1.0, y, workspace=ws)
+            ops.vq_gemm_nvfp4(xd, w, 1.0, y, workspace=ws)
     torch.cuda.current_stream().wait_stream(st)
     for i in range(4):
         y.zero_()
@@ -230,7 +276,7 @@ def test_graph_capture_and_replay():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy(), eager), i
-        ops.vq_gemm_nvfp4(xd, c, s, 1.0, y_eager, workspace=ws)  # eager work between replays
+        ops.vq_gemm_nvfp4(xd, w, 1.0, y_eager, workspace=ws)  # eager work between replays
         torch.cuda.synchronize()
 
 
@@ -238,10 +284,14 @@ def test_binding_rejects_short_workspace():
     torch, dev = torch_dev()
     ops = _ops()
     x = torch.zeros((8, 512), dtype=torch.bfloat16, device=dev)
-    c = torch.zeros((1024, 256), dtype=torch.uint8, device=dev)
-    s = torch.zeros((1024, 32), dtype=torch.uint8, device=dev)
+    w = torch.zeros(ops.packed_bytes(ops.VQ_PACK_NVFP4, 1024, 512), dtype=torch.uint8, device=dev)
     y = torch.empty((8, 1024), dtype=torch.float32, device=dev)
     ws = torch.zeros(64, dtype=torch.uint8, device=dev)
     with pytest.raises(ops.VerifyError) as ei:
-        ops.vq_gemm_nvfp4(x, c, s, 1.0, y, workspace=ws)
+        ops.vq_gemm_nvfp4(x, w, 1.0, y, workspace=ws)
     assert ei.value.status == ops.VQ_ERR_WORKSPACE
+    # packed weights one block short of the shape
+    ws = ops.workspace(ops.VQ_OP_NVFP4, 8, 1024, 512, dev)
+    with pytest.raises(ops.VerifyError) as ei:
+        ops.vq_gemm_nvfp4(x, w[:-4608], 1.0, y, workspace=ws)
+    assert ei.value.status == ops.VQ_ERR_SHAPE

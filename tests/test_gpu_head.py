@@ -22,7 +22,7 @@ def run_head(h_bits, codes, scales, ts, drafts, lanes, R, want_logits=True, ws=N
     M, K = h_bits.shape
     V = codes.shape[0]
     h = to_dev_bf16(h_bits)
-    c, s = to_dev_u8(codes), to_dev_u8(scales)
+    w = ops.pack_nvfp4(to_dev_u8(codes), to_dev_u8(scales))
     d = torch.from_numpy(np.ascontiguousarray(drafts, dtype=np.int32)).to(dev) if R > 1 else None
     ws = ws if ws is not None else ops.workspace(ops.VQ_OP_LMHEAD, M, V, K, dev)
     outs = []
@@ -32,7 +32,7 @@ def run_head(h_bits, codes, scales, ts, drafts, lanes, R, want_logits=True, ws=N
         al = torch.full((lanes,), -7, dtype=torch.int32, device=dev)
         cm = torch.full((lanes, R), -7, dtype=torch.int32, device=dev)
         lg = torch.empty((M, V), dtype=torch.float32, device=dev) if want_logits else None
-        ops.vq_lmhead_argmax_accept(h, c, s, ts, d, lanes, R, am, al, maxlogit_out=mx, commit_out=cm,
+        ops.vq_lmhead_argmax_accept(h, w, ts, V, d, lanes, R, am, al, maxlogit_out=mx, commit_out=cm,
                                     logits_out=lg, workspace=ws)
         torch.cuda.synchronize()
         outs.append(dict(argmax=am.cpu().numpy(), maxlogit=mx.cpu().numpy(), accept=al.cpu().numpy(),
@@ -70,8 +70,8 @@ def check_head(out, logits_ref, drafts, lanes, R):
 
 
 @pytest.mark.parametrize("lanes,R,V,K,ts", [
-    (1, 8, 5000, 512, 1.0), (4, 8, 3001, 256, 0.5), (2, 5, 777, 1024, 1.0), (3, 1, 100, 64, 1.0),
-    (1, 2, 64, 128, 2.0), (4, 3, 20000, 320, 1.0),
+    (1, 8, 5000, 512, 1.0), (4, 8, 3001, 256, 0.5), (2, 5, 777, 1024, 1.0), (3, 1, 100, 128, 1.0),
+    (1, 2, 64, 128, 2.0), (4, 3, 20000, 384, 1.0), (2, 4, 1111, 640, 1.0),
 ])
 def test_head_random(lanes, R, V, K, ts):
     say(f"case: head lanes={lanes} R={R} V={V} K={K}")
@@ -119,7 +119,7 @@ def test_head_exact_ties_break_to_lowest_index():
 
 
 def test_head_nan_rows_and_zero_logits():
-    lanes, R, V, K = 1, 4, 300, 64
+    lanes, R, V, K = 1, 4, 300, 128
     M = lanes * R
     h = inputs.x_bf16((201,), M, K)
     h[1, :] = 0x7FC0           # NaN row -> every logit NaN -> argmax -1
