@@ -102,7 +102,7 @@ void bind_workspace(vq::GemmParams& p, const vq::Schedule& s, void* ws) {
   p.tiles = s.tiles;
   p.iters = s.iters;
   p.total = s.total;
-  p.workers = s.workers;
+  p.wgs = s.wgs;
 }
 
 int32_t launch(int fmt, int epi, const vq::GemmParams& p, void* stream) {
@@ -120,15 +120,18 @@ Schedule make_schedule(int epi, int32_t n_out, int32_t k) {
   s.tiles = tiles_for(epi, n_out);
   s.iters = k / kIterK;
   s.total = (int64_t)s.tiles * s.iters;
-  int64_t w = (s.total + kMinItersPerWorker - 1) / kMinItersPerWorker;
-  if (w > kMaxWorkers) w = kMaxWorkers;
-  if (w < 1) w = 1;
-  s.workers = (int32_t)w;
+  // enough 4-wave workgroups to fill the chip, each wave with at least
+  // kMinItersPerWave iterations; never more workgroups than iterations
+  int64_t g = (s.total + 4 * kMinItersPerWave - 1) / (4 * kMinItersPerWave);
+  if (g > kMaxWgs) g = kMaxWgs;
+  if (g > s.total) g = s.total;
+  if (g < 1) g = 1;
+  s.wgs = (int32_t)g;
   size_t off = 0;
   s.off_zero = off;
   off += 256;
   s.off_partials = off;
-  off = align_up(off + (size_t)2 * s.workers * kSlotFloats * sizeof(float), 256);
+  off = align_up(off + (size_t)2 * s.wgs * kSlotFloats * sizeof(float), 256);
   s.off_counters = off;
   off = align_up(off + (size_t)s.tiles * sizeof(uint32_t), 256);
   if (epi == EPI_ARGMAX) {

@@ -19,10 +19,10 @@ constexpr int kIterK = 128;
 constexpr int kBlockF4 = 4096 + 512;
 constexpr int kBlockF8 = 8192;
 
-// Stream-K workers (waves) per launch at most, and the minimum iterations a
-// worker gets before the worker count is reduced.
-constexpr int kMaxWorkers = 2048;
-constexpr int kMinItersPerWorker = 4;
+// Stream-K units (workgroups of 4 waves) per launch at most, and the minimum
+// iterations per wave before the workgroup count is reduced.
+constexpr int kMaxWgs = 512;
+constexpr int kMinItersPerWave = 4;
 // Partial-sum slot: 4 sub-tiles x up to 16 accumulator registers x 64 lanes.
 constexpr int kSlotFloats = kNT * 16 * 64;
 // Argmax candidate buckets per row (spread the cross-worker atomics).
@@ -33,7 +33,7 @@ struct Schedule {
   int32_t tiles;      // T
   int32_t iters;      // I = K / kIterK
   int64_t total;      // T * I
-  int32_t workers;    // P
+  int32_t wgs;        // G: stream-K workgroups
   size_t off_zero, off_partials, off_counters, off_best, off_done, bytes;
 };
 
@@ -54,7 +54,7 @@ struct GemmParams {
   void* y;
   int32_t M, N, K;        // N: output columns
   int32_t y_f32;
-  int32_t tiles, iters, workers;
+  int32_t tiles, iters, wgs;
   int64_t total;
   const uint16_t* zeros;  // 256 bytes the kernels never write (zero-filled with the workspace)
   float* partials;

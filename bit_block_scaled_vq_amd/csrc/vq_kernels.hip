@@ -32,11 +32,13 @@
 //    scale operand, so a non-power-of-two E4M3 scale cannot be folded into it.
 //  * FP8: the MFMA accumulates directly; the per-tensor scale is applied in
 //    the epilogue.
-//  * Every wave is an independent stream-K worker over the (tile, iteration)
-//    space: worker w owns iterations [w*W/P, (w+1)*W/P). A tile split between
-//    workers is reduced by its last-arriving piece in worker order
-//    (deterministic). Cross-worker data moves only through agent-scope
-//    atomics, so no L2 write-back/invalidate is issued.
+//  * Stream-K over 4-wave workgroups: workgroup g owns iterations
+//    [g*W/G, (g+1)*W/G) of the (tile, iteration) space and each wave a
+//    contiguous quarter of that. Tiles shared by waves of one workgroup are
+//    summed through LDS; tiles shared by workgroups are reduced by the
+//    last-arriving workgroup in workgroup order (deterministic, independent of
+//    M). Cross-workgroup data moves only through agent-scope atomics, so no
+//    L2 write-back/invalidate is issued.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -119,13 +121,6 @@ __device__ __forceinline__ float key_value(unsigned long long key) {
   return key ? __uint_as_float(u) : __builtin_nanf("");
 }
 
-__device__ __forceinline__ int64_t worker_start(int64_t w, int64_t total, int64_t workers) {
-  return w * total / workers;
-}
-// The worker whose range contains iteration `it`.
-__device__ __forceinline__ int64_t worker_of(int64_t it, int64_t total, int64_t workers) {
-  return ((it + 1) * workers - 1) / total;
-}
 
 // ------------------------------------------------------------- weight pack
 //
@@ -457,28 +452,49 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int tile, int lane
   }
 }
 
-// Cross-worker data (partial sums, counters, argmax candidates) only moves
-// through agent-scope atomics: relaxed atomic stores and loads are
-// write-through / coherent at device scope, so waiting for the stores'
-// acknowledgement before the counter increment orders them, and no L2
-// write-back or invalidate is needed.
+// Cross-workgroup data (partial sums, counters, argmax candidates) only moves
+// through agent-scope atomics: relaxed atomic stores and loads are coherent at
+// device scope, so waiting for the stores' acknowledgement before the counter
+// increment orders them, and no L2 write-back or invalidate is needed.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
-// One piece of `tile` has been published; true when it was the last one, i.e.
-// the caller must reduce the pieces and finish the tile.
-__device__ __forceinline__ bool arrive(const GemmParams& p, int tile, int lane) {
-  uint32_t old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0);
-  const int64_t I = p.iters;
-  const int64_t w0 = worker_of((int64_t)tile * I, p.total, p.workers);
-  const int64_t w1 = worker_of((int64_t)(tile + 1) * I - 1, p.total, p.workers);
-  return old == (uint32_t)(w1 - w0);
+// Stream-K over workgroups: workgroup g owns iterations [g*W/G, (g+1)*W/G).
+__device__ __forceinline__ int64_t wg_start(int64_t g, const GemmParams& p) { return g * p.total / p.wgs; }
+// The workgroup whose range contains iteration `it`.
+__device__ __forceinline__ int64_t wg_of(int64_t it, const GemmParams& p) {
+  return ((it + 1) * p.wgs - 1) / p.total;
 }
 
-template <int REGS>
+// Lanes whose accumulators hold distinct sums (NVFP4: after the l / l^32
+// combine, lanes 32..63 repeat lanes 0..31 and are neither stored nor loaded).
+template <int FMT>
+__device__ __forceinline__ bool holds_sum(int lane) {
+  return FMT == FMT_FP8 || lane < 32;
+}
+
+// A piece (one wave's or one workgroup's share of a tile) is stored as value
+// (t, r) of lane l at float index (t * REGS + r) * 64 + l.
+template <int FMT, int REGS>
+__device__ __forceinline__ void lds_put(float* slot, int lane, const float (&v)[kNT][REGS]) {
+  if (!holds_sum<FMT>(lane)) return;
+#pragma unroll
+  for (int t = 0; t < kNT; ++t)
+#pragma unroll
+    for (int r = 0; r < REGS; ++r) slot[(t * REGS + r) * 64 + lane] = v[t][r];
+}
+template <int FMT, int REGS>
+__device__ __forceinline__ void lds_add(const float* slot, int lane, float (&v)[kNT][REGS]) {
+  if (!holds_sum<FMT>(lane)) return;
+#pragma unroll
+  for (int t = 0; t < kNT; ++t)
+#pragma unroll
+    for (int r = 0; r < REGS; ++r) v[t][r] += slot[(t * REGS + r) * 64 + lane];
+}
+
+template <int FMT, int REGS>
 __device__ __forceinline__ void store_piece(const GemmParams& p, int64_t slot, int lane, const float (&v)[kNT][REGS]) {
   static_assert(kNT * REGS * 64 <= kSlotFloats, "slot too small");
+  if (!holds_sum<FMT>(lane)) return;
   float* dst = p.partials + slot * kSlotFloats;
 #pragma unroll
   for (int t = 0; t < kNT; ++t)
@@ -487,24 +503,55 @@ __device__ __forceinline__ void store_piece(const GemmParams& p, int64_t slot, i
       __hip_atomic_store(&dst[(t * REGS + r) * 64 + lane], v[t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Sum of every piece of `tile`, in worker order (deterministic).
-template <int REGS>
+// One workgroup piece of `tile` has been published; true when it was the last
+// one, i.e. the caller must reduce the pieces and finish the tile.
+__device__ __forceinline__ bool arrive(const GemmParams& p, int tile, int lane) {
+  uint32_t old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
+  const int64_t t0 = (int64_t)tile * p.iters;
+  return old == (uint32_t)(wg_of(t0 + p.iters - 1, p) - wg_of(t0, p));
+}
+
+// Sum of the workgroup pieces of `tile` in workgroup order (deterministic).
+// Workgroups after the first start inside the tile (their slot 0); the first
+// one holds the tile in slot 0 only if it starts exactly at the tile's start.
+template <int FMT, int REGS>
 __device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int lane, float (&sum)[kNT][REGS]) {
-  const int64_t I = p.iters;
-  const int64_t w0 = worker_of((int64_t)tile * I, p.total, p.workers);
-  const int64_t w1 = worker_of((int64_t)(tile + 1) * I - 1, p.total, p.workers);
+  const int64_t t0 = (int64_t)tile * p.iters;
+  const int64_t g0 = wg_of(t0, p), g1 = wg_of(t0 + p.iters - 1, p);
 #pragma unroll
   for (int t = 0; t < kNT; ++t)
 #pragma unroll
     for (int r = 0; r < REGS; ++r) sum[t][r] = 0.0f;
-  for (int64_t v = w0; v <= w1; ++v) {
-    const bool vfirst = (worker_start(v, p.total, p.workers) / I) == tile;
-    const float* src = p.partials + (2 * v + (vfirst ? 0 : 1)) * kSlotFloats;
+  if (holds_sum<FMT>(lane)) {
+    const int64_t first_slot = 2 * g0 + (wg_start(g0, p) == t0 ? 0 : 1);
+    int64_t g = g0;
+    // two pieces per step: all loads of a step are in flight together
+    for (; g + 1 <= g1; g += 2) {
+      const float* a = p.partials + (g == g0 ? first_slot : 2 * g) * kSlotFloats;
+      const float* b = p.partials + 2 * (g + 1) * kSlotFloats;
+      float va[kNT][REGS], vb[kNT][REGS];
 #pragma unroll
-    for (int t = 0; t < kNT; ++t)
+      for (int t = 0; t < kNT; ++t)
 #pragma unroll
-      for (int r = 0; r < REGS; ++r)
-        sum[t][r] += __hip_atomic_load(&src[(t * REGS + r) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int r = 0; r < REGS; ++r) {
+          va[t][r] = __hip_atomic_load(&a[(t * REGS + r) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          vb[t][r] = __hip_atomic_load(&b[(t * REGS + r) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+      for (int t = 0; t < kNT; ++t)
+#pragma unroll
+        for (int r = 0; r < REGS; ++r) sum[t][r] = (sum[t][r] + va[t][r]) + vb[t][r];
+    }
+    if (g == g1) {
+      const float* a = p.partials + (g == g0 ? first_slot : 2 * g) * kSlotFloats;
+#pragma unroll
+      for (int t = 0; t < kNT; ++t)
+#pragma unroll
+        for (int r = 0; r < REGS; ++r)
+          sum[t][r] += __hip_atomic_load(&a[(t * REGS + r) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   if (lane == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -525,128 +572,168 @@ struct Occupancy {
   static constexpr int value = RG == 1 ? 2 : 1;
 };
 
+// Schedule. Workgroup g (4 waves) owns the iteration range [S, E) of the
+// (tile, iteration) space, and wave q the q-th quarter of it. A wave finishes
+// every tile that lies inside its own range. A tile shared by several waves of
+// the workgroup is summed through LDS, in wave order, by the lowest wave that
+// touches it; if the tile also extends past [S, E), that sum is the
+// workgroup's piece of the tile and goes through the global stream-K fixup,
+// whose last-arriving workgroup sums the pieces in workgroup order.
 template <int FMT, int EPI, int RG>
 __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kernel(GemmParams p) {
   using T = Traits<FMT, RG>;
   constexpr int PD = PipeDepth<FMT, RG>::value;
   constexpr int REGS = T::REGS;
+  constexpr int SLOT = kNT * REGS * 64;
   constexpr size_t BLOCK = FMT == FMT_NVFP4 ? kBlockF4 : kBlockF8;
+  __shared__ float lds[4 * SLOT];
+
   const int lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w >= p.workers) return;
-  const int64_t s = worker_start(w, p.total, p.workers);
-  const int64_t e = worker_start(w + 1, p.total, p.workers);
+  const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t g = blockIdx.x;
+  const int64_t S = wg_start(g, p), E = wg_start(g + 1, p);
+  const int64_t span = E - S;
+  const int64_t s = S + q * span / 4, e = S + (q + 1) * span / 4;
   const int I = p.iters;
-
-  // The worker's weight stream is the contiguous run of blocks [s, e).
-  const uint8_t* wnext = p.w + (size_t)s * BLOCK;
-  XCursor<FMT, RG> xc;
-  xc.init(p, lane);
-  int xkit = (int)(s % I);
-  int64_t lit = s;  // next iteration to load
-
-  WBuf<FMT> wb[PD];
-  XBuf<RG> xb[PD];
-  auto load_next = [&](int q) {
-    load_w<FMT>(wb[q], wnext, lane);
-    xc.load(xb[q], xkit);
-    if (lit + 1 < e) {  // loads past the range re-read the last iteration
-      ++lit;
-      wnext += BLOCK;
-      if (++xkit == I) xkit = 0;
-    }
-  };
-#pragma unroll
-  for (int q = 0; q < PD; ++q) load_next(q);
-
   const int first_tile = (int)(s / I);
-  int ctile = first_tile;
-  int ckit = (int)(s - (int64_t)first_tile * I);
-  bool started_inside = ckit != 0;
-  bool have_head = false;
-  Acc<FMT, RG> acc;
-  acc.zero();
+
   Best<REGS> best;
 #pragma unroll
   for (int r = 0; r < REGS; ++r) best.k[r] = 0ull;
-  int finished = 0;  // tiles finished by this worker (vocabulary head)
+  int finished = 0;       // tiles this wave finished (vocabulary head)
+  bool lds_piece = false; // this wave's share of first_tile (entered mid-way) is in its LDS slot
+  bool reg_piece = false; // acc holds this wave's share of ctile, which starts inside [s, e)
+  int ctile = first_tile;
+  Acc<FMT, RG> acc;
+  acc.zero();
 
-  auto tile_end = [&]() {
-    acc.combine();
-    if (!started_inside) {
-      epilogue<FMT, EPI, RG>(p, ctile, lane, [&](int t, int r) { return acc.get(t, r); }, best);
-      ++finished;
-    } else {
-      // the first tile was entered mid-way: park its piece now (published
-      // with the tail piece at the end of the range)
-      store_piece<REGS>(p, 2 * w, lane, acc.v);
-      have_head = true;
+  if (s < e) {
+    // The wave's weight stream is the contiguous run of blocks [s, e).
+    const uint8_t* wnext = p.w + (size_t)s * BLOCK;
+    XCursor<FMT, RG> xc;
+    xc.init(p, lane);
+    int xkit = (int)(s - (int64_t)first_tile * I);
+    int64_t lit = s;  // next iteration to load
+
+    WBuf<FMT> wb[PD];
+    XBuf<RG> xb[PD];
+    auto load_next = [&](int qq) {
+      load_w<FMT>(wb[qq], wnext, lane);
+      xc.load(xb[qq], xkit);
+      if (lit + 1 < e) {  // loads past the range re-read the last iteration
+        ++lit;
+        wnext += BLOCK;
+        if (++xkit == I) xkit = 0;
+      }
+    };
+#pragma unroll
+    for (int qq = 0; qq < PD; ++qq) load_next(qq);
+
+    int ckit = (int)(s - (int64_t)first_tile * I);
+    bool started_inside = ckit != 0;
+
+    auto tile_end = [&]() {
+      acc.combine();
+      if (!started_inside) {
+        epilogue<FMT, EPI, RG>(p, ctile, lane, [&](int t, int r) { return acc.get(t, r); }, best);
+        ++finished;
+      } else {
+        lds_put<FMT, REGS>(lds + q * SLOT, lane, acc.v);
+        lds_piece = true;
+      }
+      acc.zero();
+      started_inside = false;
+      ckit = 0;
+      ++ctile;
+    };
+
+    const int64_t count = e - s;
+    const int64_t blocks = count / PD;
+    for (int64_t bl = 0; bl < blocks; ++bl) {
+#pragma unroll
+      for (int qq = 0; qq < PD; ++qq) {
+        compute_iter<FMT, RG>(wb[qq], xb[qq], acc);
+        load_next(qq);
+        if (++ckit == I) tile_end();
+      }
     }
-    acc.zero();
-    started_inside = false;
-    ckit = 0;
-    ++ctile;
+    const int rem = (int)(count - blocks * PD);
+#pragma unroll
+    for (int qq = 0; qq < PD; ++qq) {
+      if (qq < rem) {
+        compute_iter<FMT, RG>(wb[qq], xb[qq], acc);
+        if (++ckit == I) tile_end();
+      }
+    }
+    if (ckit != 0) {  // the range ends inside ctile
+      acc.combine();
+      if (started_inside) {  // ... which is first_tile, entered mid-way
+        lds_put<FMT, REGS>(lds + q * SLOT, lane, acc.v);
+        lds_piece = true;
+      } else {
+        reg_piece = true;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Adds the LDS shares of the later waves that start inside `tile`.
+  auto add_later_waves = [&](int tile, float (&sum)[kNT][REGS]) {
+    const int64_t tend = (int64_t)(tile + 1) * I;
+    for (int q2 = q + 1; q2 < 4; ++q2) {
+      const int64_t s2 = S + q2 * span / 4, e2 = S + (q2 + 1) * span / 4;
+      if (s2 >= tend) break;
+      if (s2 < e2) lds_add<FMT, REGS>(lds + q2 * SLOT, lane, sum);
+    }
+  };
+  // Finishes `tile` from this workgroup's share: directly when the tile lies
+  // inside [S, E), else through the global fixup.
+  auto finish = [&](int tile, float (&sum)[kNT][REGS]) {
+    const int64_t t0 = (int64_t)tile * I;
+    if (t0 >= S && t0 + I <= E) {
+      epilogue<FMT, EPI, RG>(p, tile, lane, [&](int t, int r) { return sum[t][r]; }, best);
+      ++finished;
+      return;
+    }
+    store_piece<FMT, REGS>(p, 2 * g + (tile == S / I ? 0 : 1), lane, sum);
+    wait_stores();
+    if (arrive(p, tile, lane)) {
+      float tot[kNT][REGS];
+      reduce_tile<FMT, REGS>(p, tile, lane, tot);
+      epilogue<FMT, EPI, RG>(p, tile, lane, [&](int t, int r) { return tot[t][r]; }, best);
+      ++finished;
+    }
   };
 
-  const int64_t count = e - s;
-  const int64_t blocks = count / PD;
-  for (int64_t bl = 0; bl < blocks; ++bl) {
-#pragma unroll
-    for (int q = 0; q < PD; ++q) {
-      compute_iter<FMT, RG>(wb[q], xb[q], acc);
-      load_next(q);
-      if (++ckit == I) tile_end();
-    }
+  if (reg_piece) {  // this wave is the lowest one touching ctile
+    add_later_waves(ctile, acc.v);
+    finish(ctile, acc.v);
   }
-  const int rem = (int)(count - blocks * PD);
+  if (lds_piece && s == S) {  // the workgroup starts inside first_tile: its first wave collects the share
+    float sum[kNT][REGS];
 #pragma unroll
-  for (int q = 0; q < PD; ++q) {
-    if (q < rem) {
-      compute_iter<FMT, RG>(wb[q], xb[q], acc);
-      if (++ckit == I) tile_end();
-    }
-  }
-
-  // Publish the partial pieces (the first tile if it was entered mid-way, the
-  // last tile if the range ends inside it), then finish every tile whose last
-  // piece this worker delivered.
-  const bool have_tail = ckit != 0;
-  if (have_head || have_tail) {
-    if (have_tail) {
-      acc.combine();
-      store_piece<REGS>(p, 2 * w + (ctile == first_tile ? 0 : 1), lane, acc.v);
-    }
-    wait_stores();
-    const bool last_head = have_head && arrive(p, first_tile, lane);
-    const bool last_tail = have_tail && arrive(p, ctile, lane);
-    if (last_head || last_tail) {
-      float sum[kNT][REGS];
-      if (last_head) {
-        reduce_tile<REGS>(p, first_tile, lane, sum);
-        epilogue<FMT, EPI, RG>(p, first_tile, lane, [&](int t, int r) { return sum[t][r]; }, best);
-        ++finished;
-      }
-      if (last_tail) {
-        reduce_tile<REGS>(p, ctile, lane, sum);
-        epilogue<FMT, EPI, RG>(p, ctile, lane, [&](int t, int r) { return sum[t][r]; }, best);
-        ++finished;
-      }
-    }
+    for (int t = 0; t < kNT; ++t)
+#pragma unroll
+      for (int r = 0; r < REGS; ++r) sum[t][r] = 0.0f;
+    lds_add<FMT, REGS>(lds + q * SLOT, lane, sum);
+    add_later_waves(first_tile, sum);
+    finish(first_tile, sum);
   }
 
   if constexpr (EPI == EPI_ARGMAX) {
     if (finished > 0) {
 #pragma unroll
-      for (int q = 0; q < REGS; ++q) {
-        unsigned long long k = T::out_lane(lane) ? best.k[q] : 0ull;
+      for (int qq = 0; qq < REGS; ++qq) {
+        unsigned long long k = T::out_lane(lane) ? best.k[qq] : 0ull;
 #pragma unroll
         for (int off = T::RED / 2; off >= 1; off >>= 1) {
           const unsigned long long o = __shfl_xor(k, off);
           k = o > k ? o : k;
         }
-        const int m = T::row(lane, q >> 2, q & 3);
+        const int m = T::row(lane, qq >> 2, qq & 3);
         if (T::out_lane(lane) && (lane % T::RED) == 0 && m < p.M && k != 0ull) {
-          const unsigned long long prev = __hip_atomic_fetch_max(&p.best[(w % kBuckets) * kMaxRows + m], k,
+          const int bucket = (int)((g * 4 + q) % kBuckets);
+          const unsigned long long prev = __hip_atomic_fetch_max(&p.best[bucket * kMaxRows + m], k,
                                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           asm volatile("" ::"v"(prev));  // keep the returning form: it completes before the wait below
         }
@@ -683,7 +770,7 @@ template <int FMT, int EPI>
 static int launch_rg(const GemmParams& p, hipStream_t st) {
   const int rows = FMT == FMT_NVFP4 ? 8 : 16;
   const int rg = (p.M + rows - 1) / rows;
-  const dim3 grid((unsigned)((p.workers + 3) / 4)), block(256);
+  const dim3 grid((unsigned)p.wgs), block(256);
   if constexpr (FMT == FMT_NVFP4) {
     switch (rg) {
       case 1: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p); break;
