@@ -246,6 +246,64 @@ def cpu_baseline(inputs_mod, budget_s=20.0):
     }
 
 
+def kernel_source_digest():
+    """sha256 of the kernel sources: stored HBM-traffic figures apply only to
+    the kernels they were counted on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("vq_kernels.hip", "vq_internal.h"):
+        with open(os.path.join(ROOT, "bit_block_scaled_vq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel factor),
+    or None when the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "gate_up_silu_m8_traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return int(t["traffic_bytes_per_launch"])
+
+
+def pmc_workload(copies=4, reps=2):
+    """Small fixed workload for hardware-counter runs: the copy probe on
+    1 GiB (the calibration kernel of known traffic) and the dominant kernel
+    ([gate; up] + SiLU*up, M = 8) on rotating weight copies."""
+    import torch
+    from bit_block_scaled_vq_amd import inputs, ops
+    dev = torch.device("cuda:0")
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    for _ in range(reps):
+        ops.vq_probe_copy(src, dst)
+    torch.cuda.synchronize()
+    del src, dst
+    ws = []
+    for c in range(copies):
+        cc, ss = inputs.device_nvfp4_weights((5, 3000 + c), 2 * INTER, HIDDEN, dev)
+        ws.append(ops.pack_nvfp4(cc, ss, gate_up=True))
+        del cc, ss
+    x = inputs.device_x_bf16((5, 1000), M_ROWS, HIDDEN, dev)
+    h = torch.empty((M_ROWS, INTER), dtype=torch.bfloat16, device=dev)
+    work = ops.workspace(ops.VQ_OP_NVFP4_SILU_MUL, M_ROWS, INTER, HIDDEN, dev)
+    for r in range(reps):
+        for w in ws:
+            ops.vq_gemm_nvfp4(x, w, 1.0, h, epilogue=ops.VQ_EPI_SILU_MUL, workspace=work)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_workload": {"copy_probe_bytes_each": nbytes, "copy_probe_launches": reps,
+                                       "gate_up_launches": reps * copies,
+                                       "gate_up_weight_bytes": weight_bytes("nvfp4_silu", INTER, HIDDEN),
+                                       "gate_up_activation_bytes": act_bytes(INTER, HIDDEN)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,7 +311,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="run only the small hardware-counter workload (copy probe + dominant kernel)")
     args = ap.parse_args()
+    if args.pmc_workload:
+        pmc_workload()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the verify-pass weight stream is built and timed on a single "
               f"MI355X (asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr)
@@ -348,7 +411,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": stored_traffic(),
             "avg_launch_us": round(dom_s * 1e6, 2),
             "bytes_per_launch": gu_w + gu_a,
         },
