@@ -126,6 +126,18 @@ Schedule make_schedule(int epi, int32_t n_out, int32_t k) {
   if (g > kMaxWgs) g = kMaxWgs;
   if (g > s.total) g = s.total;
   if (g < 1) g = 1;
+  // Wide outputs: whole tiles per workgroup (no cross-workgroup fixup) when a
+  // divisor of the tile count gives an even load over the CUs: one workgroup
+  // per CU on at least 3/4 of them, or two per CU on at least 7/8 of them.
+  for (int64_t k = 1; k <= 64 && s.tiles >= kMaxWgs / 4; ++k) {
+    if (s.tiles % k) continue;
+    const int64_t ga = s.tiles / k;
+    if ((ga >= kCUs * 3 / 4 && ga <= kCUs) || (ga >= 2 * kCUs * 7 / 8 && ga <= 2 * kCUs)) {
+      g = ga;
+      break;
+    }
+    if (ga < kCUs * 3 / 4) break;
+  }
   s.wgs = (int32_t)g;
   size_t off = 0;
   s.off_zero = off;

@@ -22,6 +22,7 @@ constexpr int kBlockF8 = 8192;
 // Stream-K units (workgroups of 4 waves) per launch at most, and the minimum
 // iterations per wave before the workgroup count is reduced.
 constexpr int kMaxWgs = 512;
+constexpr int kCUs = 256;  // MI355X compute units
 constexpr int kMinItersPerWave = 4;
 // Partial-sum slot: 4 sub-tiles x up to 16 accumulator registers x 64 lanes.
 constexpr int kSlotFloats = kNT * 16 * 64;
