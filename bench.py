@@ -272,10 +272,10 @@ def stored_traffic():
     return int(t["traffic_bytes_per_launch"])
 
 
-def pmc_workload(copies=4, reps=2):
+def pmc_workload(m_rows=M_ROWS, copies=4, reps=2):
     """Small fixed workload for hardware-counter runs: the copy probe on
     1 GiB (the calibration kernel of known traffic) and the dominant kernel
-    ([gate; up] + SiLU*up, M = 8) on rotating weight copies."""
+    ([gate; up] + SiLU*up, M = m_rows) on rotating weight copies."""
     import torch
     from bit_block_scaled_vq_amd import inputs, ops
     dev = torch.device("cuda:0")
@@ -291,17 +291,17 @@ def pmc_workload(copies=4, reps=2):
         cc, ss = inputs.device_nvfp4_weights((5, 3000 + c), 2 * INTER, HIDDEN, dev)
         ws.append(ops.pack_nvfp4(cc, ss, gate_up=True))
         del cc, ss
-    x = inputs.device_x_bf16((5, 1000), M_ROWS, HIDDEN, dev)
-    h = torch.empty((M_ROWS, INTER), dtype=torch.bfloat16, device=dev)
-    work = ops.workspace(ops.VQ_OP_NVFP4_SILU_MUL, M_ROWS, INTER, HIDDEN, dev)
+    x = inputs.device_x_bf16((5, 1000), m_rows, HIDDEN, dev)
+    h = torch.empty((m_rows, INTER), dtype=torch.bfloat16, device=dev)
+    work = ops.workspace(ops.VQ_OP_NVFP4_SILU_MUL, m_rows, INTER, HIDDEN, dev)
     for r in range(reps):
         for w in ws:
             ops.vq_gemm_nvfp4(x, w, 1.0, h, epilogue=ops.VQ_EPI_SILU_MUL, workspace=work)
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_workload": {"copy_probe_bytes_each": nbytes, "copy_probe_launches": reps,
+    print(json.dumps({"pmc_workload": {"rows": m_rows, "copy_probe_bytes_each": nbytes, "copy_probe_launches": reps,
                                        "gate_up_launches": reps * copies,
                                        "gate_up_weight_bytes": weight_bytes("nvfp4_silu", INTER, HIDDEN),
-                                       "gate_up_activation_bytes": act_bytes(INTER, HIDDEN)}}), flush=True)
+                                       "gate_up_activation_bytes": act_bytes(INTER, HIDDEN, m_rows)}}), flush=True)
 
 
 def main():
@@ -313,9 +313,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--pmc-workload", action="store_true",
                     help="run only the small hardware-counter workload (copy probe + dominant kernel)")
+    ap.add_argument("--pmc-rows", type=int, default=M_ROWS, help="activation rows M of the counter workload")
     args = ap.parse_args()
     if args.pmc_workload:
-        pmc_workload()
+        pmc_workload(args.pmc_rows)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the verify-pass weight stream is built and timed on a single "
