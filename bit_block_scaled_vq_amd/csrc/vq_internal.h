@@ -6,7 +6,11 @@
 
 namespace vq {
 
-enum Fmt : int { FMT_NVFP4 = 0, FMT_FP8 = 1 };
+// FMT_NVFP4: block scale applied to the fp32 partial after the MFMA (two
+// scale blocks per MFMA through zero-padded activation rows; up to 8 rows per
+// row group). FMT_NVFP4S: the same packed weights scaled in registers before
+// the MFMA (exact in bf16), 16 activation rows per row group.
+enum Fmt : int { FMT_NVFP4 = 0, FMT_FP8 = 1, FMT_NVFP4S = 2 };
 enum Epi : int { EPI_NONE = 0, EPI_SILU = 1, EPI_ARGMAX = 2 };
 
 // Packed weights are laid out in blocks of one tile (64 weight rows, four

@@ -69,6 +69,26 @@ __device__ __forceinline__ bf16x8_t dec_fp4x8(uint32_t w) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
+// 8 E2M1 codes (one dword, low nibble first) times one E4M3 block scale ->
+// 8 bf16 in k order. Every E2M1 x E4M3 product has at most 6 significant bits
+// and lies inside bf16's normal range, so each product is exact in bf16.
+__device__ __forceinline__ bf16x8_t dec_fp4x8_scaled(uint32_t w, float sc) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  u32x4_t r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f32x2_t v = b == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
+              : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
+              : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
+                       : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    v.x = v.x * sc;
+    v.y = v.y * sc;
+    r[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  }
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
 // 8 E4M3FN codes (two dwords, byte order = k order) -> 8 bf16.
 __device__ __forceinline__ bf16x8_t dec_fp8x8(uint32_t lo, uint32_t hi) {
   auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -218,7 +238,7 @@ template <int FMT, int RG>
 struct Traits {
   static constexpr int REGS = 4 * RG;  // accumulator registers per sub-tile
   static constexpr int RED = 16;       // lanes holding the same output rows
-  static __device__ __forceinline__ bool out_lane(int lane) { return FMT == FMT_FP8 || lane < 32; }
+  static __device__ __forceinline__ bool out_lane(int lane) { return FMT != FMT_NVFP4 || lane < 32; }
   // output row of accumulator register (rg, r) of this lane
   static __device__ __forceinline__ int row(int lane, int rg, int r) {
     if (FMT == FMT_NVFP4) return 8 * rg + 4 * ((lane >> 4) & 1) + r;
@@ -242,6 +262,8 @@ struct WBuf<FMT_NVFP4> {
   u32x4_t s;       // per sub-tile: the 4 block scales of this lane's half
 };
 template <>
+struct WBuf<FMT_NVFP4S> : WBuf<FMT_NVFP4> {};
+template <>
 struct WBuf<FMT_FP8> {
   u32x4_t c[kNT][2];  // per sub-tile: weights of MFMA steps (0,1) and (2,3)
 };
@@ -252,7 +274,7 @@ struct XBuf {
 
 template <int FMT>
 __device__ __forceinline__ void load_w(WBuf<FMT>& b, const uint8_t* blk, int lane) {
-  if constexpr (FMT == FMT_NVFP4) {
+  if constexpr (FMT != FMT_FP8) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) b.c[t] = ld16(blk + t * 1024 + lane * 16);
     b.s = ld16(blk + 4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
@@ -331,6 +353,21 @@ __device__ __forceinline__ void compute_iter(const WBuf<FMT>& b, const XBuf<RG>&
                                                                     f32x4_t{}, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc.v[t][4 * rg + r] = __builtin_fmaf(sc, d[r], acc.v[t][4 * rg + r]);
+        }
+      }
+    }
+  } else if constexpr (FMT == FMT_NVFP4S) {
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t wv = dec_fp4x8_scaled(b.c[t][j], scale_byte(b.s[t], j));
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          f32x4_t a = {acc.v[t][4 * rg], acc.v[t][4 * rg + 1], acc.v[t][4 * rg + 2], acc.v[t][4 * rg + 3]};
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[rg][j]), wv, a, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc.v[t][4 * rg + r] = a[r];
         }
       }
     }
@@ -469,7 +506,7 @@ __device__ __forceinline__ int64_t wg_of(int64_t it, const GemmParams& p) {
 // combine, lanes 32..63 repeat lanes 0..31 and are neither stored nor loaded).
 template <int FMT>
 __device__ __forceinline__ bool holds_sum(int lane) {
-  return FMT == FMT_FP8 || lane < 32;
+  return FMT != FMT_NVFP4 || lane < 32;
 }
 
 // A piece (one wave's or one workgroup's share of a tile) is stored as value
@@ -585,7 +622,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
   constexpr int PD = PipeDepth<FMT, RG>::value;
   constexpr int REGS = T::REGS;
   constexpr int SLOT = kNT * REGS * 64;
-  constexpr size_t BLOCK = FMT == FMT_NVFP4 ? kBlockF4 : kBlockF8;
+  constexpr size_t BLOCK = FMT == FMT_FP8 ? kBlockF8 : kBlockF4;
   __shared__ float lds[4 * SLOT];
 
   const int lane = threadIdx.x & 63;
@@ -787,6 +824,12 @@ static int launch_rg(const GemmParams& p, hipStream_t st) {
 
 int launch_gemm(int fmt, int epi, const GemmParams& p, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (fmt == FMT_NVFP4 && p.M > 8) {
+    // more than 8 rows: scale in registers, 16 activation rows per MFMA
+    if (epi == EPI_NONE) return launch_rg<FMT_NVFP4S, EPI_NONE>(p, st);
+    if (epi == EPI_SILU) return launch_rg<FMT_NVFP4S, EPI_SILU>(p, st);
+    return launch_rg<FMT_NVFP4S, EPI_ARGMAX>(p, st);
+  }
   if (fmt == FMT_NVFP4) {
     if (epi == EPI_NONE) return launch_rg<FMT_NVFP4, EPI_NONE>(p, st);
     if (epi == EPI_SILU) return launch_rg<FMT_NVFP4, EPI_SILU>(p, st);

@@ -61,8 +61,12 @@
  *     may run concurrently need distinct workspaces. A NULL or short workspace
  *     returns VQ_ERR_WORKSPACE; the schedule never changes silently.
  *   - Results are deterministic: the K partition and the order of the fixed
- *     split-K reduction depend only on (N, K) and the epilogue, never on M,
- *     so row r of an M-row call equals row r of any other M bit for bit.
+ *     split-K reduction depend only on (N, K) and the epilogue, never on M.
+ *     FP8: row r of an M-row call equals row r of any other M bit for bit.
+ *     NVFP4 has two compute families with different rounding (M <= 8: the
+ *     block scale multiplies each block's fp32 partial sum; M > 8: the weights
+ *     are scaled before the MFMA, exactly, and summed in fp32), and rows agree
+ *     bit for bit within a family.
  *   - The first call on a device checks that it is gfx950 (VQ_ERR_DEVICE).
  *     A failed launch returns VQ_ERR_LAUNCH.
  *   - Thread-safe; vq_last_error() is per host thread.

@@ -209,8 +209,9 @@ def test_fp8_all_codes_one_hot():
 # ---------------------------------------------- properties of the schedule
 
 def test_rows_independent_of_m_and_deterministic():
-    # the K partition and the reduction order depend only on (N, K): the rows
-    # shared by calls with different M are bitwise equal.
+    # the K partition and the reduction order depend only on (N, K) and the
+    # NVFP4 compute family (M <= 8: block scale after the MFMA; M > 8: weights
+    # scaled before it): rows shared by calls of one family are bitwise equal.
     torch, dev = torch_dev()
     ops = _ops()
     n, k = 5120, 17408        # the narrow, long-K down projection shape
@@ -224,7 +225,9 @@ def test_rows_independent_of_m_and_deterministic():
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         ops.vq_gemm_nvfp4(to_dev_bf16(x32[:m]), w, 1.0, y, workspace=ws)
         outs[m] = y.cpu().numpy()
-    for m in (1, 5, 8, 9, 16, 24):
+    for m in (1, 5):
+        assert np.array_equal(outs[m], outs[8][:m]), m
+    for m in (9, 16, 24):
         assert np.array_equal(outs[m], outs[32][:m]), m
     y2 = torch.empty((32, n), dtype=torch.float32, device=dev)
     ops.vq_gemm_nvfp4(to_dev_bf16(x32), w, 1.0, y2, workspace=ws)
