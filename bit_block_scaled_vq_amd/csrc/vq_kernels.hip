@@ -600,13 +600,15 @@ __device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int l
 // would cap the weight prefetch at its depth).
 template <int FMT, int RG>
 struct PipeDepth {
-  static constexpr int value = RG <= 2 ? 3 : 2;  // wide row groups: the X ring would spill
+  // wide row groups: the X ring would spill; scaled NVFP4 with two row groups
+  // trades ring depth for a second wave per SIMD (measured faster)
+  static constexpr int value = (FMT == FMT_NVFP4S && RG == 2) ? 2 : (RG <= 2 ? 3 : 2);
 };
 // Waves per SIMD: one row group keeps two waves per SIMD; more row groups keep
 // one wave per SIMD so the extra accumulators and X fragments stay in registers.
 template <int FMT, int RG>
 struct Occupancy {
-  static constexpr int value = RG == 1 ? 2 : 1;
+  static constexpr int value = (RG == 1 || (FMT == FMT_NVFP4S && RG == 2)) ? 2 : 1;
 };
 
 // Schedule. Workgroup g (4 waves) owns the iteration range [S, E) of the
