@@ -120,23 +120,27 @@ Schedule make_schedule(int epi, int32_t n_out, int32_t k) {
   s.tiles = tiles_for(epi, n_out);
   s.iters = k / kIterK;
   s.total = (int64_t)s.tiles * s.iters;
-  // enough 4-wave workgroups to fill the chip, each wave with at least
-  // kMinItersPerWave iterations; never more workgroups than iterations
+  // Stream-K over at most kMaxWgs 4-wave workgroups, each wave with at least
+  // kMinItersPerWave iterations; never more workgroups than iterations.
   int64_t g = (s.total + 4 * kMinItersPerWave - 1) / (4 * kMinItersPerWave);
   if (g > kMaxWgs) g = kMaxWgs;
   if (g > s.total) g = s.total;
   if (g < 1) g = 1;
-  // Wide outputs: whole tiles per workgroup (no cross-workgroup fixup) when a
-  // divisor of the tile count gives an even load over the CUs: one workgroup
-  // per CU on at least 3/4 of them, or two per CU on at least 7/8 of them.
-  for (int64_t k = 1; k <= 64 && s.tiles >= kMaxWgs / 4; ++k) {
-    if (s.tiles % k) continue;
-    const int64_t ga = s.tiles / k;
-    if ((ga >= kCUs * 3 / 4 && ga <= kCUs) || (ga >= 2 * kCUs * 7 / 8 && ga <= 2 * kCUs)) {
-      g = ga;
+  // Prefer a tile-aligned split that keeps at least 7/8 of the CUs busy with
+  // one workgroup each: k workgroups per tile (narrow outputs) or k tiles per
+  // workgroup (wide ones). Then no workgroup holds parts of two tiles, and a
+  // tile's shares come from whole workgroups.
+  const int64_t lo = kCUs * 7 / 8;
+  if (s.tiles <= kCUs) {
+    const int64_t k = kCUs / s.tiles;
+    if (k >= 1 && s.tiles * k >= lo && s.iters / k >= 4 * kMinItersPerWave) g = s.tiles * k;
+  } else {
+    for (int64_t k = (s.tiles + kCUs - 1) / kCUs; k <= 64; ++k) {
+      if (s.tiles % k) continue;
+      if (s.tiles / k < lo) break;
+      g = s.tiles / k;
       break;
     }
-    if (ga < kCUs * 3 / 4) break;
   }
   s.wgs = (int32_t)g;
   size_t off = 0;

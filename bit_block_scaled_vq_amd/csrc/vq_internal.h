@@ -23,10 +23,11 @@ constexpr int kIterK = 128;
 constexpr int kBlockF4 = 4096 + 512;
 constexpr int kBlockF8 = 8192;
 
-// Stream-K units (workgroups of 4 waves) per launch at most, and the minimum
-// iterations per wave before the workgroup count is reduced.
-constexpr int kMaxWgs = 512;
+// Minimum iterations per wave before the workgroup count is reduced.
 constexpr int kCUs = 256;  // MI355X compute units
+// Unaligned stream-K splits use one CU per XCD fewer than the chip has
+// (measured faster than all 256 for the 34816 x 5120 projection).
+constexpr int kMaxWgs = kCUs - 8;
 constexpr int kMinItersPerWave = 4;
 // Partial-sum slot: 4 sub-tiles x up to 16 accumulator registers x 64 lanes.
 constexpr int kSlotFloats = kNT * 16 * 64;
