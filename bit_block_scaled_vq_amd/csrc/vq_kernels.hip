@@ -553,6 +553,7 @@ __device__ __forceinline__ bool arrive(const GemmParams& p, int tile, int lane) 
 // Sum of the workgroup pieces of `tile` in workgroup order (deterministic).
 // Workgroups after the first start inside the tile (their slot 0); the first
 // one holds the tile in slot 0 only if it starts exactly at the tile's start.
+// Up to B pieces are loaded per step (one round trip for the usual 2-4).
 template <int FMT, int REGS>
 __device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int lane, float (&sum)[kNT][REGS]) {
   const int64_t t0 = (int64_t)tile * p.iters;
@@ -563,31 +564,30 @@ __device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int l
     for (int r = 0; r < REGS; ++r) sum[t][r] = 0.0f;
   if (holds_sum<FMT>(lane)) {
     const int64_t first_slot = 2 * g0 + (wg_start(g0, p) == t0 ? 0 : 1);
-    int64_t g = g0;
-    // two pieces per step: all loads of a step are in flight together
-    for (; g + 1 <= g1; g += 2) {
-      const float* a = p.partials + (g == g0 ? first_slot : 2 * g) * kSlotFloats;
-      const float* b = p.partials + 2 * (g + 1) * kSlotFloats;
-      float va[kNT][REGS], vb[kNT][REGS];
+    constexpr int B = REGS <= 4 ? 4 : 2;
+    for (int64_t gb = g0; gb <= g1; gb += B) {
+      float v[B][kNT][REGS];
 #pragma unroll
-      for (int t = 0; t < kNT; ++t)
+      for (int b = 0; b < B; ++b) {
+        if (gb + b <= g1) {  // uniform
+          const int64_t gg = gb + b;
+          const float* a = p.partials + (gg == g0 ? first_slot : 2 * gg) * kSlotFloats;
 #pragma unroll
-        for (int r = 0; r < REGS; ++r) {
-          va[t][r] = __hip_atomic_load(&a[(t * REGS + r) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          vb[t][r] = __hip_atomic_load(&b[(t * REGS + r) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int t = 0; t < kNT; ++t)
+#pragma unroll
+            for (int r = 0; r < REGS; ++r)
+              v[b][t][r] = __hip_atomic_load(&a[(t * REGS + r) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+      }
 #pragma unroll
-      for (int t = 0; t < kNT; ++t)
+      for (int b = 0; b < B; ++b) {
+        if (gb + b <= g1) {
 #pragma unroll
-        for (int r = 0; r < REGS; ++r) sum[t][r] = (sum[t][r] + va[t][r]) + vb[t][r];
-    }
-    if (g == g1) {
-      const float* a = p.partials + (g == g0 ? first_slot : 2 * g) * kSlotFloats;
+          for (int t = 0; t < kNT; ++t)
 #pragma unroll
-      for (int t = 0; t < kNT; ++t)
-#pragma unroll
-        for (int r = 0; r < REGS; ++r)
-          sum[t][r] += __hip_atomic_load(&a[(t * REGS + r) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int r = 0; r < REGS; ++r) sum[t][r] += v[b][t][r];
+        }
+      }
     }
   }
   if (lane == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
