@@ -200,6 +200,44 @@ def dominant_kernel_duration(torch, p, reps=3):
     return e0.elapsed_time(e1) / (reps * len(idx)) * 1e-3   # seconds
 
 
+def m_sweep(torch, ops, inputs_mod, p, rows=(1, 8, 16, 24, 32), reps=2):
+    """Weight GB/s per launch of the four repeated projection shapes at each
+    row count (1-4 lanes of 8 verify rows), rotating over the pass's layers so
+    no launch finds its weights in a cache."""
+    dev = p.dev
+    kinds = {"mlp_gate_up": "nvfp4_silu", "mlp_down": "nvfp4", "gdn_in": "fp8", "gdn_out": "fp8"}
+    out = {}
+    for m in rows:
+        res = {}
+        for kind, fmt in kinds.items():
+            idx = [i for i, it in enumerate(p.items) if it[0] == kind]
+            _, _, n, k = p.items[idx[0]]
+            x = inputs_mod.device_x_bf16((5, 4000, m, k), m, k, dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            op = {"fp8": ops.VQ_OP_FP8, "nvfp4": ops.VQ_OP_NVFP4, "nvfp4_silu": ops.VQ_OP_NVFP4_SILU_MUL}[fmt]
+            ws = p.ws[(op, n, k)]
+
+            def run(i):
+                if fmt == "fp8":
+                    ops.vq_gemm_fp8(x, p.w[i], 1.0, y, workspace=ws)
+                else:
+                    ops.vq_gemm_nvfp4(x, p.w[i], 1.0, y, epilogue=ops.VQ_EPI_SILU_MUL if fmt == "nvfp4_silu"
+                                      else ops.VQ_EPI_NONE, workspace=ws)
+            for i in idx[:2]:
+                run(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                for i in idx:
+                    run(i)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * len(idx))
+            res[kind] = round(weight_bytes(fmt, n, k) / (us * 1e-6) / 1e9, 1)
+        out[str(m)] = res
+    return out
+
+
 def cpu_baseline(inputs_mod, budget_s=20.0):
     """The oracle, as it stands, on a bounded sample of the same workload:
     4096-row slices of an NVFP4 gate/up matrix and of an FP8 GDN in-projection
@@ -367,6 +405,7 @@ def main():
     eager_ms = (time.perf_counter() - t0) * 1e3
     kinds = per_kind_durations(torch, p)
     dom_s = dominant_kernel_duration(torch, p)
+    sweep = m_sweep(torch, ops, inputs, p)
     gu_w = weight_bytes("nvfp4_silu", INTER, HIDDEN)
     gu_a = act_bytes(INTER, HIDDEN)
     achieved = (gu_w + gu_a) / dom_s / 1e9
@@ -405,6 +444,7 @@ def main():
         "eager_ms_per_pass": round(eager_ms, 3),
         "accept_len_last_pass": accept,
         "kernels": kinds,
+        "m_sweep_weight_gbps": sweep,
         "roofline": {
             "kernel": "vq_gemm_kernel<NVFP4, SILU_MUL, M<=8> ([gate;up] 34816x5120 + SiLU*up)",
             "bound": "hbm",
