@@ -298,3 +298,33 @@ def test_binding_rejects_short_workspace():
     with pytest.raises(ops.VerifyError) as ei:
         ops.vq_gemm_nvfp4(x, w[:-4608], 1.0, y, workspace=ws)
     assert ei.value.status == ops.VQ_ERR_SHAPE
+
+
+# ------------------------------------------- model shapes, as bench.py runs them
+
+@pytest.mark.parametrize("n,k", [(16384, 5120), (14336, 5120), (5120, 6144)])
+@pytest.mark.parametrize("m", [8, 32])
+def test_fp8_model_shapes_full_size(n, k, m):
+    # GDN in-projection (256 workgroups, one tile each), attention q+gate+k+v
+    # (224, one tile each) and the out-projections (240, three per tile)
+    say(f"case: FP8 full size M={m} N={n} K={k}")
+    key = (110, n, k)
+    x = inputs.x_bf16(key + (m,), m, k)
+    w = inputs.fp8_weights(key, n, k)
+    ref = O.gemm_fp8(x, w, 0.75)
+    r = run_fp8(x, w, 0.75)
+    check_f32(r["f32"], ref, what=f"fp8 {n}x{k} M{m}")
+    check_bf16_store(r["bf16"], r["f32"], ref)
+
+
+@pytest.mark.parametrize("m", [16, 32])
+def test_mlp_gate_up_full_size_wide_rows(m):
+    # the weights-scaled-in-registers NVFP4 family (M > 8) on the [gate; up] shape
+    say(f"case: [gate;up] 34816x5120 + SiLU*up at M={m}")
+    inter, hid = 17408, 5120
+    x = inputs.x_bf16((111, m), m, hid)
+    gu_c, gu_s = inputs.nvfp4_weights((2, 0), 2 * inter, hid)
+    h_ref, _ = O.mlp_silu_mul(x, gu_c, gu_s, 1.0, inter)
+    r = run_nvfp4(x, gu_c, gu_s, 1.0, inter, epi=1)
+    check_f32(r["f32"], h_ref, what=f"h M{m}")
+    check_bf16_store(r["bf16"], r["f32"], h_ref)
