@@ -5,3 +5,4 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 its Python binding) never imports, links or calls anything under ``oracle/``.
 """
 from .verify_oracle import *  # noqa: F401,F403
+from .sampling_oracle import *  # noqa: F401,F403
