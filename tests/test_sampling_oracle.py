@@ -12,7 +12,6 @@ from scipy import special, stats
 import oracle as O
 
 
-
 def _rng(*key):
     return np.random.default_rng(list(key))
 
@@ -104,7 +103,7 @@ def test_draw_distribution():
     assert stats.chisquare(obs, n * p).pvalue > 1e-4
 
 
-def _spec_first_tokens(seed, n, res_fn=None):
+def _spec_first_tokens(seed, n):
     ids, p, q_ids, q = _target_and_draft(seed)
     rng = _rng(seed, 1)
     d = rng.choice(q_ids, size=n, p=q)  # the draft token is a sample of q
