@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 #include <string>
 
@@ -160,6 +161,24 @@ Schedule make_schedule(int epi, int32_t n_out, int32_t k) {
   return s;
 }
 
+SampleLayout make_sample_layout(int32_t M, int32_t V) {
+  SampleLayout L{};
+  L.chunks = (V + kSampleChunk - 1) / kSampleChunk;
+  size_t off = 0;
+  L.off_cand = off;
+  off = align_up(off + (size_t)M * L.chunks * 4 * kTopK * sizeof(unsigned long long), 256);
+  L.off_ids = off;
+  off = align_up(off + (size_t)M * kTopK * sizeof(int32_t), 256);
+  L.off_probs = off;
+  off = align_up(off + (size_t)M * kTopK * sizeof(float), 256);
+  L.off_meta = off;
+  off = align_up(off + (size_t)M * 2 * sizeof(int32_t), 256);
+  L.off_count = off;
+  off = align_up(off + 4 * sizeof(uint32_t), 256);
+  L.bytes = off;
+  return L;
+}
+
 }  // namespace vq
 
 extern "C" {
@@ -183,6 +202,10 @@ const char* vq_status_str(int32_t s) {
 }
 
 size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K) {
+  if (op == VQ_OP_SAMPLE) {
+    if (M < 1 || M > vq::kMaxRows || N < 1 || N > vq::kMaxSampleV) return 0;
+    return vq::make_sample_layout(M, N).bytes;
+  }
   if (!shape_ok(M, N, K)) return 0;
   switch (op) {
     case VQ_OP_NVFP4: return vq::make_schedule(vq::EPI_NONE, N, K).bytes;
@@ -356,6 +379,67 @@ int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* w, size_t w_by
   p.commit_out = commit_out;
   bind_workspace(p, s, workspace);
   return launch(vq::FMT_NVFP4, vq::EPI_ARGMAX, p, stream);
+}
+
+int32_t vq_sample_accept(const float* logits, int32_t lanes, int32_t R, int32_t V, float temperature, int32_t top_k,
+                         float top_p, const int32_t* draft, const int32_t* draft_ids, const float* draft_probs,
+                         const float* u_accept, const float* u_draw, int32_t* token_out, int32_t* accept_len_out,
+                         int32_t* commit_out, int32_t* cand_out, float* prob_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!logits || !u_draw || !accept_len_out)
+    return fail(VQ_ERR_NULL, "vq_sample_accept: logits, u_draw and accept_len_out are required");
+  if (lanes < 1 || lanes > 4) return fail(VQ_ERR_SHAPE, "lanes = %d outside [1, 4]", lanes);
+  if (R < 1 || R > 8) return fail(VQ_ERR_SHAPE, "R = %d outside [1, 8]", R);
+  if (V < 1 || V > vq::kMaxSampleV) return fail(VQ_ERR_SHAPE, "V = %d outside [1, %d]", V, vq::kMaxSampleV);
+  if (R > 1 && !draft) return fail(VQ_ERR_NULL, "draft is required when R > 1");
+  if ((draft_ids == nullptr) != (draft_probs == nullptr))
+    return fail(VQ_ERR_NULL, "draft_ids and draft_probs go together (both or neither)");
+  if (draft_ids && !u_accept) return fail(VQ_ERR_NULL, "u_accept is required with draft distributions");
+  if (!(temperature > 0.0f) || !std::isfinite(temperature))
+    return fail(VQ_ERR_VALUE, "temperature must be finite and > 0 (greedy verify is vq_lmhead_argmax_accept)");
+  if (top_k < 1 || top_k > vq::kTopK) return fail(VQ_ERR_VALUE, "top_k = %d outside [1, %d]", top_k, vq::kTopK);
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(VQ_ERR_VALUE, "top_p must lie in (0, 1]");
+  const void* arrays[] = {logits, draft, draft_ids, draft_probs, u_accept, u_draw,
+                          token_out, accept_len_out, commit_out, cand_out, prob_out};
+  for (const void* a : arrays)
+    if (a && !aligned(a, 4)) return fail(VQ_ERR_ALIGN, "int32/float arrays must be 4-byte aligned");
+  const int32_t M = lanes * R;
+  const vq::SampleLayout L = vq::make_sample_layout(M, V);
+  if (!workspace) return fail(VQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.bytes);
+  if (!aligned(workspace, 16)) return fail(VQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (workspace_bytes < L.bytes)
+    return fail(VQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.bytes);
+  int32_t st = check_device();
+  if (st) return st;
+  char* base = static_cast<char*>(workspace);
+  vq::SampleParams p{};
+  p.logits = logits;
+  p.M = M;
+  p.V = V;
+  p.lanes = lanes;
+  p.R = R;
+  p.chunks = L.chunks;
+  p.temperature = temperature;
+  p.top_k = top_k;
+  p.top_p = top_p;
+  p.draft = draft;
+  p.q_ids = draft_ids;
+  p.q_probs = draft_probs;
+  p.u_accept = u_accept;
+  p.u_draw = u_draw;
+  p.token_out = token_out;
+  p.accept_len_out = accept_len_out;
+  p.commit_out = commit_out;
+  p.cand_out = cand_out;
+  p.prob_out = prob_out;
+  p.cand = reinterpret_cast<unsigned long long*>(base + L.off_cand);
+  p.row_ids = reinterpret_cast<int32_t*>(base + L.off_ids);
+  p.row_probs = reinterpret_cast<float*>(base + L.off_probs);
+  p.row_meta = reinterpret_cast<int32_t*>(base + L.off_meta);
+  p.lane_count = reinterpret_cast<uint32_t*>(base + L.off_count);
+  const int err = vq::launch_sample(p, stream);
+  if (err != 0) return fail(VQ_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));
+  return VQ_OK;
 }
 
 int32_t vq_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {

@@ -84,9 +84,45 @@ struct PackParams {
   int32_t tiles, iters;
 };
 
+// Sampled verify over fp32 logits [M][V]: per row the top-32 candidates, the
+// truncated target distribution, a draw, and the accept scan per lane.
+constexpr int kSampleChunk = 8192;   // logits per chunk workgroup (32 per thread)
+constexpr int kTopK = 32;            // largest top_k
+constexpr int kDraftCands = 16;      // draft (id, prob) pairs per verify row
+constexpr int kMaxSampleV = 1 << 20; // at most 128 chunks per row
+
+struct SampleLayout {
+  int32_t chunks;                    // C = ceil(V / kSampleChunk)
+  size_t off_cand, off_ids, off_probs, off_meta, off_count, bytes;
+};
+SampleLayout make_sample_layout(int32_t M, int32_t V);
+
+struct SampleParams {
+  const float* logits;               // [M][V]
+  int32_t M, V, lanes, R, chunks;
+  float temperature, top_p;
+  int32_t top_k;
+  const int32_t* draft;              // [lanes][R-1]
+  const int32_t* q_ids;              // [lanes][R-1][16] or null (point-mass)
+  const float* q_probs;
+  const float* u_accept;             // [M]
+  const float* u_draw;               // [M]
+  int32_t* token_out;                // [M] or null
+  int32_t* accept_len_out;           // [lanes]
+  int32_t* commit_out;               // [lanes][R] or null
+  int32_t* cand_out;                 // [M][32] or null
+  float* prob_out;                   // [M][32] or null
+  unsigned long long* cand;          // workspace: [M][C][4][32] chunk candidates
+  int32_t* row_ids;                  // workspace: [M][32]
+  float* row_probs;                  // workspace: [M][32]
+  int32_t* row_meta;                 // workspace: [M][2] (kept count, draw)
+  uint32_t* lane_count;              // workspace: [4] rows finished per lane
+};
+
 // Launchers: return 0 on success, else the hipError_t of the launch.
 int launch_gemm(int fmt, int epi, const GemmParams& p, void* stream);
 int launch_pack(int fmt, const PackParams& p, void* stream);
+int launch_sample(const SampleParams& p, void* stream);
 int launch_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 int launch_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 

@@ -38,6 +38,11 @@ T_CODES = 1
 T_SCALES = 2
 T_FP8 = 3
 T_DRAFT = 4
+T_LOGITS = 5
+T_UNIFORM = 6
+T_DRAFT_Q = 7
+
+LOGIT_STD = 2.5
 
 SCALE_STD = 0.05
 FP8_STD = 0.02
@@ -127,6 +132,38 @@ def drafts(key, argmax_rows: np.ndarray, vocab: int, p: float = DRAFT_P) -> np.n
     u = g.random((lanes, r - 1))
     rand_ids = g.integers(0, vocab, size=(lanes, r - 1))
     return np.where(u < p, a[:, : r - 1], rand_ids).astype(np.int32)
+
+
+def logits_f32(key, m: int, v: int, std: float = LOGIT_STD) -> np.ndarray:
+    """Verify logits [m][v] (float32), N(0, std^2)."""
+    return (rng(*key, T_LOGITS).standard_normal((m, v), dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+def uniforms(key, *shape: int) -> np.ndarray:
+    """float32 uniforms in [0, 1)."""
+    return rng(*key, T_UNIFORM).random(shape, dtype=np.float32)
+
+
+def draft_distributions(key, preferred, vocab: int, n: int = 16):
+    """Draft distributions for a batch of verify rows: preferred [rows][P]
+    token ids (P >= n // 2; -1 entries are skipped). Returns (ids [rows][n]
+    int32, probs [rows][n] float32, tokens [rows] int32): per row n // 2 ids
+    from its preferred list, the rest uniform over [0, vocab) (a repeat of an
+    earlier id is allowed; the first occurrence counts), Dirichlet(1)
+    probabilities, and one token drawn from them."""
+    pref = np.atleast_2d(np.asarray(preferred, dtype=np.int64))
+    rows = pref.shape[0]
+    g = rng(*key, T_DRAFT_Q)
+    ids = np.empty((rows, n), dtype=np.int32)
+    probs = np.empty((rows, n), dtype=np.float32)
+    toks = np.empty(rows, dtype=np.int32)
+    for r in range(rows):
+        cand = pref[r][pref[r] >= 0]
+        take = g.choice(cand, size=min(n // 2, cand.size), replace=False) if cand.size else np.empty(0, np.int64)
+        ids[r] = np.concatenate([take, g.integers(0, vocab, size=n - take.size)])
+        probs[r] = g.dirichlet(np.ones(n)).astype(np.float32)
+        toks[r] = ids[r][g.choice(n, p=probs[r].astype(np.float64) / probs[r].astype(np.float64).sum())]
+    return ids, probs, toks
 
 
 # -------------------------------------------------------------- device side

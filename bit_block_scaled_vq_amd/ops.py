@@ -31,13 +31,14 @@ VQ_OP_NVFP4 = 0
 VQ_OP_NVFP4_SILU_MUL = 1
 VQ_OP_FP8 = 2
 VQ_OP_LMHEAD = 3
+VQ_OP_SAMPLE = 4
 VQ_PACK_NVFP4 = 0
 VQ_PACK_NVFP4_GATE_UP = 1
 VQ_PACK_FP8 = 2
 
 EXPORTS = [
     "vq_packed_bytes", "vq_pack_nvfp4", "vq_pack_fp8",
-    "vq_gemm_nvfp4", "vq_gemm_fp8", "vq_lmhead_argmax_accept", "vq_workspace_bytes",
+    "vq_gemm_nvfp4", "vq_gemm_fp8", "vq_lmhead_argmax_accept", "vq_sample_accept", "vq_workspace_bytes",
     "vq_status_str", "vq_last_error", "vq_abi_version", "vq_probe_copy", "vq_probe_read",
 ]
 
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.vq_lmhead_argmax_accept.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, i32,
                                           vp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.vq_lmhead_argmax_accept.restype = i32
+    L.vq_sample_accept.argtypes = [vp, i32, i32, i32, f32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.vq_sample_accept.restype = i32
     L.vq_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.vq_workspace_bytes.restype = sz
     L.vq_status_str.argtypes = [i32]
@@ -257,6 +260,41 @@ def vq_lmhead_argmax_accept(h, w, tensor_scale: float, V: int, draft, lanes: int
         _ptr(h), _ptr(w), w.numel(), float(tensor_scale), _ptr(draft), lanes, R, V, K,
         _ptr(argmax_out), _ptr(maxlogit_out), _ptr(accept_len_out), _ptr(commit_out),
         _ptr(logits_out), ld, ws_ptr, ws_n, _stream(stream)))
+
+
+def vq_sample_accept(logits, lanes: int, R: int, temperature: float, top_k: int, top_p: float, u_draw,
+                     accept_len_out, draft=None, draft_ids=None, draft_probs=None, u_accept=None,
+                     token_out=None, commit_out=None, cand_out=None, prob_out=None, workspace=None, stream=None):
+    """Sampled verify over fp32 logits [lanes*R][V]: truncated target
+    distribution per row, a draw with u_draw, and the accept scan per lane
+    (point-mass rule without draft_ids/draft_probs, speculative sampling with
+    them). Results stay on the device."""
+    torch = _torch()
+    _need(logits, "logits", (torch.float32,), 2)
+    M, V = logits.shape
+    if M != lanes * R:
+        raise ValueError("logits must have lanes * R rows")
+    _need(u_draw, "u_draw", (torch.float32,))
+    _need(accept_len_out, "accept_len_out", (torch.int32,))
+    if u_draw.numel() != M or accept_len_out.numel() != lanes:
+        raise ValueError("u_draw must hold lanes * R values and accept_len_out lanes")
+    for name, t, dt, n in (("draft", draft, torch.int32, lanes * (R - 1)),
+                           ("draft_ids", draft_ids, torch.int32, lanes * (R - 1) * 16),
+                           ("draft_probs", draft_probs, torch.float32, lanes * (R - 1) * 16),
+                           ("u_accept", u_accept, torch.float32, M),
+                           ("token_out", token_out, torch.int32, M),
+                           ("commit_out", commit_out, torch.int32, lanes * R),
+                           ("cand_out", cand_out, torch.int32, M * 32),
+                           ("prob_out", prob_out, torch.float32, M * 32)):
+        if t is not None:
+            _need(t, name, (dt,))
+            if t.numel() != n:
+                raise ValueError(f"{name} must hold {n} values")
+    ws_ptr, ws_n = _ws(workspace)
+    _check(lib().vq_sample_accept(
+        _ptr(logits), lanes, R, V, float(temperature), int(top_k), float(top_p), _ptr(draft), _ptr(draft_ids),
+        _ptr(draft_probs), _ptr(u_accept), _ptr(u_draw), _ptr(token_out), _ptr(accept_len_out),
+        _ptr(commit_out), _ptr(cand_out), _ptr(prob_out), ws_ptr, ws_n, _stream(stream)))
 
 
 def vq_probe_copy(src, dst, stream=None):

@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define VQ_ABI_VERSION 2
+#define VQ_ABI_VERSION 3
 
 typedef enum {
   VQ_OK = 0,
@@ -96,7 +96,7 @@ typedef enum {
 
 typedef enum { VQ_OUT_BF16 = 0, VQ_OUT_F32 = 1 } vq_out_dtype;
 typedef enum { VQ_EPI_NONE = 0, VQ_EPI_SILU_MUL = 1 } vq_epilogue;
-typedef enum { VQ_OP_NVFP4 = 0, VQ_OP_NVFP4_SILU_MUL = 1, VQ_OP_FP8 = 2, VQ_OP_LMHEAD = 3 } vq_op;
+typedef enum { VQ_OP_NVFP4 = 0, VQ_OP_NVFP4_SILU_MUL = 1, VQ_OP_FP8 = 2, VQ_OP_LMHEAD = 3, VQ_OP_SAMPLE = 4 } vq_op;
 typedef enum { VQ_PACK_NVFP4 = 0, VQ_PACK_NVFP4_GATE_UP = 1, VQ_PACK_FP8 = 2 } vq_pack_kind;
 
 /* Bytes of the packed form of a canonical matrix of `rows` rows and K columns
@@ -173,10 +173,66 @@ int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* w, size_t w_by
                                 void* logits_out, int32_t logits_dtype,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Sampled verify over the fp32 verify logits (nonzero temperature): per row
+ * the target's distribution, a draw from it, and the accept scan per lane.
+ * ("144 tok/s needs 502 GB/s ...", section "Exact, up to top-32": the
+ * distribution is temperature over the row's first top_k <= 32 logits,
+ * truncated by top_p and renormalised, and acceptance is the speculative-
+ * sampling test u*q < p with a draw from max(p - q, 0) on rejection;
+ * "Beating Splash on an M5 Max ...", section "What actually moved the
+ * needle": top-k, top-p, sampling and acceptance run on the GPU and write a
+ * small result block; "lithos-metal ...", section "How DSpark is wired in":
+ * the point-mass case, where the draft token is accepted only when it equals
+ * the target's draw.)
+ *   logits   fp32 [M][V], M = lanes * R, rows grouped by lane as in
+ *            vq_lmhead_argmax_accept (its logits_out in VQ_OUT_F32)
+ *   temperature > 0 and finite; 1 <= top_k <= 32; 0 < top_p <= 1
+ *   Per row: candidates in logit order (equal logits by lower id, -0 == +0,
+ *   NaN never a candidate); w_i = exp((z_i - z_0) / temperature) over the
+ *   first top_k; kept = the shortest prefix whose weight reaches top_p of the
+ *   total (zero weights dropped); probabilities w_i / sum(kept). A row whose
+ *   top logit is not finite has no distribution (draw -1, kept count 0).
+ *   u_draw   fp32 [M] uniforms in [0, 1): row r's draw is the first kept
+ *            candidate whose cumulative weight exceeds u_draw[r] of the kept
+ *            weight (the last kept one if none)
+ *   draft    int32 [lanes][R-1] drafted tokens (draft j of lane l is checked
+ *            at row l*R + j); required when R > 1
+ *   draft_ids, draft_probs  int32 / fp32 [lanes][R-1][16], or both NULL.
+ *            NULL selects the point-mass rule: draft j is accepted when it
+ *            equals row j's draw, and the first differing draw is the bonus.
+ *            Given, they are the draft's distribution q_j for row j (id -1 =
+ *            empty slot; the first pair with a matching id counts; other
+ *            tokens have q = 0) and the speculative-sampling rule applies:
+ *            accept draft j when u_accept[row] * q_j(d_j) < p_j(d_j); on the
+ *            first rejection the token is drawn with u_draw[row] from
+ *            max(p_j - q_j, 0) over the kept candidates (from p_j when that
+ *            has no mass). With every draft accepted the bonus is the last
+ *            row's draw.
+ *   u_accept fp32 [M] uniforms (speculative-sampling rule only; entries of
+ *            the last row of a lane are not read)
+ *   token_out      int32 [M] or NULL: each row's draw (-1: no distribution)
+ *   accept_len_out int32 [lanes]: committed tokens, in [1, R]
+ *   commit_out     int32 [lanes][R] or NULL: committed tokens, -1 after them
+ *                  (and for a row without a distribution, which ends the scan)
+ *   cand_out, prob_out int32 / fp32 [M][32] or NULL: the kept candidates and
+ *                  their probabilities per row, -1 / 0 after the kept count
+ * Uniforms outside [0, 1) give unspecified tokens (never a fault). Shapes:
+ * 1 <= lanes <= 4, 1 <= R <= 8, 1 <= V <= 2^20. Workspace:
+ * vq_workspace_bytes(VQ_OP_SAMPLE, M, V, 0). Two launches on `stream`;
+ * arithmetic is fp32 with sums in a fixed order (deterministic). */
+int32_t vq_sample_accept(const float* logits, int32_t lanes, int32_t R, int32_t V,
+                         float temperature, int32_t top_k, float top_p,
+                         const int32_t* draft, const int32_t* draft_ids, const float* draft_probs,
+                         const float* u_accept, const float* u_draw,
+                         int32_t* token_out, int32_t* accept_len_out, int32_t* commit_out,
+                         int32_t* cand_out, float* prob_out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes needed by `op` at this shape (for VQ_OP_NVFP4_SILU_MUL, N is
  * the output width, i.e. half the weight rows; for VQ_OP_LMHEAD, N = V and
  * M = lanes * R). Returns 0 for an invalid shape. The size does not depend
- * on M beyond the M <= 32 bound, so one workspace serves every M. */
+ * on M beyond the M <= 32 bound, so one workspace serves every M; for
+ * VQ_OP_SAMPLE, N = V, K is ignored and the size grows with M. */
 size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K);
 
 const char* vq_status_str(int32_t status);

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = ops.lib()
-    assert L.vq_abi_version() == 2
+    assert L.vq_abi_version() == 3
     assert ops.status_str(ops.VQ_OK) == "VQ_OK"
     assert ops.status_str(ops.VQ_ERR_WORKSPACE) == "VQ_ERR_WORKSPACE"
     assert ops.status_str(99) == "VQ_ERR_UNKNOWN"
@@ -99,6 +99,45 @@ def test_lmhead_validation():
     assert _head(wsn=8) == ops.VQ_ERR_WORKSPACE
 
 
+def _sample(lg=A, lanes=1, R=8, V=1000, t=1.0, k=32, tp=0.9, draft=A, qi=None, qp=None, ua=None, ud=A,
+            al=A, ws=A, wsn=1 << 30):
+    return ops.lib().vq_sample_accept(lg, lanes, R, V, t, k, tp, draft, qi, qp, ua, ud, None, al, None, None,
+                                      None, ws, wsn, None)
+
+
+def test_sample_validation():
+    nan, inf = float("nan"), float("inf")
+    assert _sample(lg=None) == ops.VQ_ERR_NULL
+    assert _sample(ud=None) == ops.VQ_ERR_NULL
+    assert _sample(al=None) == ops.VQ_ERR_NULL
+    assert _sample(draft=None) == ops.VQ_ERR_NULL
+    assert _sample(qi=A) == ops.VQ_ERR_NULL          # ids without probs
+    assert _sample(qi=A, qp=A) == ops.VQ_ERR_NULL    # speculative rule without u_accept
+    assert _sample(lanes=5) == ops.VQ_ERR_SHAPE
+    assert _sample(R=0) == ops.VQ_ERR_SHAPE
+    assert _sample(V=0) == ops.VQ_ERR_SHAPE
+    assert _sample(V=(1 << 20) + 1) == ops.VQ_ERR_SHAPE
+    for t in (0.0, -1.0, nan, inf):
+        assert _sample(t=t) == ops.VQ_ERR_VALUE
+    assert _sample(k=0) == ops.VQ_ERR_VALUE and _sample(k=33) == ops.VQ_ERR_VALUE
+    for tp in (0.0, 1.5, nan):
+        assert _sample(tp=tp) == ops.VQ_ERR_VALUE
+    assert _sample(lg=A + 2) == ops.VQ_ERR_ALIGN
+    assert _sample(ws=None) == ops.VQ_ERR_WORKSPACE
+    assert _sample(wsn=64) == ops.VQ_ERR_WORKSPACE
+    assert _sample(R=1, draft=None, ws=None) == ops.VQ_ERR_WORKSPACE  # R = 1 needs no draft
+
+
+def test_sample_workspace_bytes():
+    L = ops.lib()
+    assert L.vq_workspace_bytes(ops.VQ_OP_SAMPLE, 0, 1000, 0) == 0
+    assert L.vq_workspace_bytes(ops.VQ_OP_SAMPLE, 33, 1000, 0) == 0
+    assert L.vq_workspace_bytes(ops.VQ_OP_SAMPLE, 8, (1 << 20) + 1, 0) == 0
+    # chunk candidate lists: ceil(V / 8192) chunks x 4 waves x 32 keys of 8 bytes per row
+    assert L.vq_workspace_bytes(ops.VQ_OP_SAMPLE, 8, 248320, 0) >= 8 * 31 * 4 * 32 * 8
+    assert L.vq_workspace_bytes(ops.VQ_OP_SAMPLE, 32, 248320, 0) > L.vq_workspace_bytes(ops.VQ_OP_SAMPLE, 8, 248320, 0)
+
+
 def test_workspace_bytes():
     L = ops.lib()
     assert L.vq_workspace_bytes(ops.VQ_OP_NVFP4, 0, 10, 128) == 0
@@ -157,6 +196,7 @@ def test_valid_call_without_gpu_reports_device_error():
     assert _nvfp4() == ops.VQ_ERR_DEVICE
     assert ops.lib().vq_pack_fp8(A, 64, 128, A, 1 << 30, None) == ops.VQ_ERR_DEVICE
     assert ops.lib().vq_probe_copy(A, A, 1024, None) == ops.VQ_ERR_DEVICE
+    assert _sample() == ops.VQ_ERR_DEVICE
 
 
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
