@@ -238,6 +238,100 @@ def m_sweep(torch, ops, inputs_mod, p, rows=(1, 8, 16, 24, 32), reps=2):
     return out
 
 
+def sampled_verify(torch, ops, inputs_mod, p, g_steps=10, reps=20):
+    """The end of the pass at nonzero temperature (temperature 1, top_k 32,
+    top_p 0.95): the head also writes fp32 logits and vq_sample_accept reads
+    them (point-mass rule; the speculative-sampling rule timed beside it).
+    Returns kernel times from HIP events on the launch stream and the graph
+    time of the whole sampled pass."""
+    import numpy as np
+    dev = p.dev
+    M, V = M_ROWS, VOCAB
+    head = len(p.items) - 1
+    logits = torch.empty((M, V), dtype=torch.float32, device=dev)
+    ws_s = ops.workspace(ops.VQ_OP_SAMPLE, M, V, 0, dev)
+    ws_h = p.ws[(ops.VQ_OP_LMHEAD, V, HIDDEN)]
+    u = torch.from_numpy(inputs_mod.uniforms((5, 3000), M)).to(dev)
+    ua = torch.from_numpy(inputs_mod.uniforms((5, 3001), M)).to(dev)
+    tok = torch.empty(M, dtype=torch.int32, device=dev)
+    acc = torch.empty(1, dtype=torch.int32, device=dev)
+    commit = torch.empty((1, M), dtype=torch.int32, device=dev)
+    # draft distributions: 16 candidates per row around the target's argmax
+    q_ids = torch.from_numpy(inputs_mod.rng(5, 3002).integers(0, V, (1, M - 1, 16), dtype=np.int32)).to(dev)
+    q_ids[:, :, 0] = p.argmax[: M - 1].view(1, M - 1)
+    q_p = torch.full((1, M - 1, 16), 1.0 / 16, dtype=torch.float32, device=dev)
+
+    def head_logits():
+        ops.vq_lmhead_argmax_accept(p.h_final, p.w[head], 1.0, V, p.drafts, 1, M, p.argmax, p.accept,
+                                    maxlogit_out=p.maxlogit, commit_out=p.commit, logits_out=logits, workspace=ws_h)
+
+    def sample():
+        ops.vq_sample_accept(logits, 1, M, 1.0, 32, 0.95, u, acc, draft=p.drafts, token_out=tok,
+                             commit_out=commit, workspace=ws_s)
+
+    def sample_spec():
+        ops.vq_sample_accept(logits, 1, M, 1.0, 32, 0.95, u, acc, draft=p.drafts, draft_ids=q_ids,
+                             draft_probs=q_p, u_accept=ua, token_out=tok, commit_out=commit, workspace=ws_s)
+
+    def timed(fn):
+        # `reps` calls captured in one graph, so the host's launch cost (tens
+        # of microseconds per call from Python) does not hide the kernels
+        fn()
+        torch.cuda.synchronize()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(gr, stream=st):
+                for _ in range(reps):
+                    fn()
+        torch.cuda.current_stream().wait_stream(st)
+        gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    head_greedy_us = timed(lambda: p.launch(head))
+    head_logits_us = timed(head_logits)
+    sample_us = timed(sample)
+    spec_us = timed(sample_spec)
+
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for i in range(head):
+                p.launch(i)
+            head_logits()
+            sample()
+    torch.cuda.current_stream().wait_stream(st)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(g_steps):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / g_steps
+    lb = M * V * 4
+    return {
+        "temperature": 1.0, "top_k": 32, "top_p": 0.95, "rule": "point-mass (graph); speculative timed alone",
+        "ms_per_pass_sampled": round(dt * 1e3, 4),
+        "weight_gbps_sampled": round(p.weight_bytes / dt / 1e9, 1),
+        "head_greedy_us": round(head_greedy_us, 2),
+        "head_with_fp32_logits_us": round(head_logits_us, 2),
+        "sampler_us": round(sample_us, 2),
+        "sampler_spec_us": round(spec_us, 2),
+        "sampler_logit_bytes": lb,
+        "sampler_logit_gbps": round(lb / (sample_us * 1e-6) / 1e9, 1),
+        "accept_len_last": int(acc.item()),
+    }
+
+
 def cpu_baseline(inputs_mod, budget_s=20.0):
     """The oracle, as it stands, on a bounded sample of the same workload:
     4096-row slices of an NVFP4 gate/up matrix and of an FP8 GDN in-projection
@@ -289,7 +383,7 @@ def kernel_source_digest():
     the kernels they were counted on."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("vq_kernels.hip", "vq_internal.h"):
+    for f in ("vq_kernels.hip", "vq_internal.h", "vq_keys.h"):
         with open(os.path.join(ROOT, "bit_block_scaled_vq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -406,6 +500,8 @@ def main():
     kinds = per_kind_durations(torch, p)
     dom_s = dominant_kernel_duration(torch, p)
     sweep = m_sweep(torch, ops, inputs, p)
+    sampled = sampled_verify(torch, ops, inputs, p)
+    log(f"sampled verify: pass {sampled['ms_per_pass_sampled']:.3f} ms, sampler {sampled['sampler_us']:.1f} us")
     gu_w = weight_bytes("nvfp4_silu", INTER, HIDDEN)
     gu_a = act_bytes(INTER, HIDDEN)
     achieved = (gu_w + gu_a) / dom_s / 1e9
@@ -445,6 +541,7 @@ def main():
         "accept_len_last_pass": accept,
         "kernels": kinds,
         "m_sweep_weight_gbps": sweep,
+        "sampled_verify": sampled,
         "roofline": {
             "kernel": "vq_gemm_kernel<NVFP4, SILU_MUL, M<=8> ([gate;up] 34816x5120 + SiLU*up)",
             "bound": "hbm",

@@ -18,11 +18,10 @@
 //    then the lower token id), so the order is total and ties break by id.
 //  * Top-32 of a row in two launches. A chunk workgroup (8192 logits, 32 per
 //    lane) reduces each wave's 2048 logits to its 32 largest keys; a row
-//    workgroup merges the chunks' lists. Inside a wave: the 32nd largest of
-//    the 64 lane maxima bounds the wave's 32nd largest key from below, so
-//    only keys at or above it can matter; they are fed to a running list, one
-//    per lane per round (a 64-key bitonic sort across lanes and a bitonic
-//    merge with the list). Random logits take one or two rounds.
+//    workgroup merges the chunks' sorted lists, one list per lane. Inside a
+//    wave, the 32nd largest lane maximum bounds the answer from below; the
+//    keys above it are packed into LDS and sorted 64 at a time (usually
+//    once).
 //  * The distribution, the draw and the accept scan run on one wave with the
 //    32 candidates in lanes 0..31; sums and prefix sums use a fixed shuffle
 //    order, so results do not depend on timing.
@@ -72,31 +71,70 @@ __device__ __forceinline__ u64 merge_top32(u64 list, u64 s, int lane) {
   return x;
 }
 
-// The wave's 32 largest keys among N per lane (0 = no key), descending in
-// lanes 0..31; lanes 32..63 return 0.
-template <int N>
-__device__ __forceinline__ u64 wave_top32(const u64 (&k)[N], int lane) {
-  static_assert(N <= 64, "one survivor bit per key");
-  u64 mx = 0;
+// The need-th largest of the wave's J * 64 values v (the largest t with at
+// least `need` values >= t), by a bitwise search on ballots.
+template <int J>
+__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&v)[J], int need) {
+  uint32_t t = 0;
 #pragma unroll
-  for (int i = 0; i < N; ++i) mx = kmax(mx, k[i]);
-  // The lane maxima are 64 of the wave's keys, so their 32nd largest is at
-  // most the wave's 32nd largest: every key of the answer is >= theta.
-  const u64 theta = __shfl(wave_sort_desc(mx, lane), 31);
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) n += (int)__popcll(__ballot(v[j] >= c));
+    if (n >= need) t = c;
+  }
+  return t;
+}
+
+// The wave's 32 largest keys among N per lane (0 = no key), descending in
+// lanes 0..31; lanes 32..63 return 0. `buf` is this wave's LDS area of 64 * N
+// keys. Every wave of the workgroup must call it (it holds a barrier).
+//
+// theta = the 32nd largest value among a sample of the keys: each lane's
+// maximum (SORTED = false), or the first four keys of each lane (SORTED =
+// true: each lane holds a descending list). At least 32 keys have value bits
+// >= theta, so every key of the answer does too; keys below it are dropped.
+// The survivors are packed into LDS and reduced 64 at a time: a bitonic sort
+// across the lanes and a bitonic merge into the running list. Random logits
+// leave 40-50 survivors: one sort.
+template <int N, bool SORTED>
+__device__ __forceinline__ u64 wave_top32(const u64 (&k)[N], int lane, u64* buf) {
+  uint32_t theta;
+  if constexpr (SORTED) {
+    const uint32_t v[4] = {(uint32_t)(k[0] >> 32), (uint32_t)(k[1] >> 32), (uint32_t)(k[2] >> 32),
+                           (uint32_t)(k[3] >> 32)};
+    theta = kth_largest<4>(v, 32);
+  } else {
+    uint32_t mh[1] = {0};
+#pragma unroll
+    for (int i = 0; i < N; ++i) mh[0] = max(mh[0], (uint32_t)(k[i] >> 32));
+    theta = kth_largest<1>(mh, 32);
+  }
   u64 live = 0;
 #pragma unroll
   for (int i = 0; i < N; ++i)
-    if (k[i] != 0ull && k[i] >= theta) live |= 1ull << i;
-  u64 list = 0;
-  while (__ballot(live != 0ull)) {
-    u64 c = 0;
+    if (k[i] != 0ull && (uint32_t)(k[i] >> 32) >= theta) live |= 1ull << i;
+  int total = 0;
+  while (true) {
+    const u64 has = __ballot(live != 0ull);
+    if (!has) break;
     if (live) {
       const int b = __builtin_ctzll(live);
       live &= live - 1;
+      u64 c = 0;
 #pragma unroll
       for (int i = 0; i < N; ++i) c = i == b ? k[i] : c;
+      buf[total + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(has >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)has, 0u))] = c;
     }
-    list = merge_top32(list, wave_sort_desc(c, lane), lane);
+    total += (int)__popcll(has);
+  }
+  __syncthreads();
+  u64 list = 0;
+  for (int base = 0; base < total; base += 64) {
+    const u64 c = base + lane < total ? buf[base + lane] : 0ull;
+    const u64 sorted = wave_sort_desc(c, lane);
+    list = base == 0 ? sorted : merge_top32(list, sorted, lane);
   }
   return lane < 32 ? list : 0ull;
 }
@@ -125,54 +163,116 @@ __device__ __forceinline__ int first_above(float cum, float t, int lane, int cou
 
 // ------------------------------------------------------------ chunk top-32
 
+// Chunk lists of a row: 4C lists of 32 keys (list L = 4 * chunk + wave). Row
+// wave w reads lists [wC, (w+1)C), one per lane; key i of list wC + l is
+// stored at i * C + l of that wave's block, so each of its loads is one
+// contiguous run.
+__device__ __forceinline__ size_t cand_index(int C, int m, int L, int i) {
+  return (size_t)m * 4 * C * 32 + (size_t)(L / C) * 32 * C + (size_t)i * C + (L % C);
+}
+
+// VEC = 4: 16-byte loads (rows 16-byte aligned, V % 4 == 0), lane l holding
+// logits 4(64i + l) .. +3 of its wave's 2048; VEC = 1: 4-byte loads.
+template <int VEC>
 __global__ __launch_bounds__(256) void sample_chunk_kernel(SampleParams p) {
+  __shared__ u64 buf[4][64 * 32];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = blockIdx.x, m = blockIdx.y;
   const float* row = p.logits + (size_t)m * p.V;
   const int64_t base = (int64_t)c * kSampleChunk + w * (kSampleChunk / 4);
   u64 k[32];
+  if constexpr (VEC == 4) {
+    float4 v[8];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int64_t idx = base + i * 64 + lane;
-    k[i] = idx < p.V ? argmax_key(row[idx], (uint32_t)idx) : 0ull;
+    for (int i = 0; i < 8; ++i) {
+      const int64_t idx = base + 4 * (i * 64 + lane);
+      v[i] = idx < p.V ? *reinterpret_cast<const float4*>(row + idx) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t idx = base + 4 * (i * 64 + lane);
+      const bool in = idx < p.V;
+      k[4 * i + 0] = in ? argmax_key(v[i].x, (uint32_t)idx) : 0ull;
+      k[4 * i + 1] = in ? argmax_key(v[i].y, (uint32_t)(idx + 1)) : 0ull;
+      k[4 * i + 2] = in ? argmax_key(v[i].z, (uint32_t)(idx + 2)) : 0ull;
+      k[4 * i + 3] = in ? argmax_key(v[i].w, (uint32_t)(idx + 3)) : 0ull;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int64_t idx = base + i * 64 + lane;
+      k[i] = idx < p.V ? argmax_key(row[idx], (uint32_t)idx) : 0ull;
+    }
   }
-  const u64 top = wave_top32<32>(k, lane);
-  if (lane < 32) p.cand[(((size_t)m * p.chunks + c) * 4 + w) * 32 + lane] = top;
+  const u64 top = wave_top32<32, false>(k, lane, buf[w]);
+  if (lane < 32) p.cand[cand_index(p.chunks, m, c * 4 + w, lane)] = top;
 }
 
 // ------------------------------------------------- row distribution + scan
 
-// Accept scan of lane l (one wave; every row of the lane is published).
+// Accept scan of lane l (one wave; every row of the lane is published). All
+// loads are issued up front (one round trip): lane j < R reads row j's kept
+// count and draw; for the speculative rule lane i also reads candidate i of
+// rows 0..R-2 and lane e < 16 the draft pair e of those rows.
 __device__ void lane_scan(const SampleParams& p, int l, int lane) {
   const int R = p.R;
+  const bool spec = p.q_ids != nullptr;
   auto ld_i = [](const int32_t* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   auto ld_f = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  int acc_len = R;
-  int commit = -1;  // lane j < R holds committed token j
-  int j = 0;
-  for (; j < R - 1; ++j) {
-    const int m = l * R + j;
-    const int count = ld_i(&p.row_meta[2 * m]);
-    const int tok = ld_i(&p.row_meta[2 * m + 1]);
-    const int d = p.draft[l * (R - 1) + j];
-    if (count == 0) break;  // no distribution: the scan stops, committing nothing here
-    if (!p.q_ids) {         // point-mass: the draft must equal the target's draw
-      if (tok == d) {
-        if (lane == j) commit = d;
-        continue;
+  int cnt_l = 0, tok_l = -1;
+  if (lane < R) {
+    cnt_l = ld_i(&p.row_meta[2 * (l * R + lane)]);
+    tok_l = ld_i(&p.row_meta[2 * (l * R + lane) + 1]);
+  }
+  int ids[7], qids[7], drafts[7];
+  float prs[7], qps[7];
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const bool row = j < R - 1;
+    drafts[j] = row ? p.draft[l * (R - 1) + j] : -1;
+    ids[j] = -1;
+    prs[j] = 0.0f;
+    qids[j] = -1;
+    qps[j] = 0.0f;
+    if (spec && row) {
+      const int m = l * R + j;
+      if (lane < 32) {
+        ids[j] = ld_i(&p.row_ids[m * 32 + lane]);
+        prs[j] = ld_f(&p.row_probs[m * 32 + lane]);
       }
-      if (lane == j) commit = tok;
-      break;
+      if (lane < kDraftCands) {
+        qids[j] = p.q_ids[(l * (R - 1) + j) * kDraftCands + lane];
+        qps[j] = p.q_probs[(l * (R - 1) + j) * kDraftCands + lane];
+      }
     }
-    const int id = lane < count ? ld_i(&p.row_ids[m * 32 + lane]) : -1;
-    const float pr = lane < count ? ld_f(&p.row_probs[m * 32 + lane]) : 0.0f;
-    const int qbase = (l * (R - 1) + j) * kDraftCands;
-    const int qid = lane < kDraftCands ? p.q_ids[qbase + lane] : -1;
-    const float qp = lane < kDraftCands ? p.q_probs[qbase + lane] : 0.0f;
-    const u64 pm = __ballot(lane < count && id == d);
-    const float pd = pm ? __shfl(pr, __builtin_ctzll(pm)) : 0.0f;
-    const u64 qm = __ballot(lane < kDraftCands && qid >= 0 && qid == d);
-    const float qd = qm ? __shfl(qp, __builtin_ctzll(qm)) : 0.0f;
+  }
+  int commit = -1;  // lane j < R holds committed token j
+  int stop = R - 1; // the row where the scan ends
+  bool done = false;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    if (done || j >= R - 1) continue;
+    const int m = l * R + j;
+    const int count = __shfl(cnt_l, j);
+    const int tok = __shfl(tok_l, j);
+    const int d = drafts[j];
+    if (count == 0) {  // no distribution: the scan stops, committing nothing here
+      stop = j;
+      done = true;
+      continue;
+    }
+    if (!spec) {  // point-mass: the draft must equal the target's draw
+      if (lane == j) commit = tok;
+      if (tok != d) {
+        stop = j;
+        done = true;
+      }
+      continue;
+    }
+    const u64 pm = __ballot(lane < count && ids[j] == d);
+    const float pd = pm ? __shfl(prs[j], __builtin_ctzll(pm)) : 0.0f;
+    const u64 qm = __ballot(lane < kDraftCands && qids[j] >= 0 && qids[j] == d);
+    const float qd = qm ? __shfl(qps[j], __builtin_ctzll(qm)) : 0.0f;
     if (p.u_accept[m] * qd < pd) {
       if (lane == j) commit = d;
       continue;
@@ -182,48 +282,44 @@ __device__ void lane_scan(const SampleParams& p, int l, int lane) {
     bool found = false;
 #pragma unroll
     for (int e = 0; e < kDraftCands; ++e) {
-      const int qe = __shfl(qid, e);
-      const float pe = __shfl(qp, e);
-      if (!found && qe >= 0 && qe == id) {
+      const int qe = __shfl(qids[j], e);
+      const float pe = __shfl(qps[j], e);
+      if (!found && qe >= 0 && qe == ids[j]) {
         qi = pe;
         found = true;
       }
     }
-    const float r = lane < count ? fmaxf(pr - qi, 0.0f) : 0.0f;
+    const float r = lane < count ? fmaxf(prs[j] - qi, 0.0f) : 0.0f;
     const float rs = wave_sum32(r);
-    int pick;
-    if (rs > 0.0f) {
-      pick = __shfl(id, first_above(wave_scan32(r, lane), p.u_draw[m] * rs, lane, count));
-    } else {
-      pick = tok;  // no residual mass: the draw from p itself
-    }
+    const int pick = rs > 0.0f ? __shfl(ids[j], first_above(wave_scan32(r, lane), p.u_draw[m] * rs, lane, count))
+                               : tok;  // no residual mass: the draw from p itself
     if (lane == j) commit = pick;
-    break;
+    stop = j;
+    done = true;
   }
-  if (j == R - 1) {  // every draft accepted: the bonus is the last row's draw
-    const int tok = ld_i(&p.row_meta[2 * (l * R + j) + 1]);
-    if (lane == j) commit = tok;
-  }
-  acc_len = j + 1;
+  if (!done && lane == R - 1) commit = tok_l;  // every draft accepted: the last row's draw is the bonus
+  const int acc_len = stop + 1;
   if (lane == 0) p.accept_len_out[l] = acc_len;
   if (p.commit_out && lane < R) p.commit_out[l * R + lane] = lane < acc_len ? commit : -1;
 }
 
+// Row workgroup: the 4C chunk lists of row m (sorted, 32 keys each); wave w
+// takes lists [w*C, (w+1)*C), one whole list per lane (two when C > 64).
 template <int NL>
 __global__ __launch_bounds__(256) void sample_row_kernel(SampleParams p) {
+  __shared__ u64 buf[4][64 * NL];
   __shared__ u64 lists[4][32];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int m = blockIdx.x;
-  // wave w merges chunk lists [w*C, (w+1)*C) of this row: C * 32 keys
-  const int n = p.chunks * 32;
-  const u64* src = p.cand + ((size_t)m * p.chunks * 4 + (size_t)w * p.chunks) * 32;
+  const int C = p.chunks;
   u64 k[NL];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int idx = i * 64 + lane;
-    k[i] = idx < n ? src[idx] : 0ull;
+  for (int h = 0; h < NL / 32; ++h) {
+    const int l = lane + 64 * h;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) k[32 * h + i] = l < C ? p.cand[cand_index(C, m, w * C + l, i)] : 0ull;
   }
-  const u64 top = wave_top32<NL>(k, lane);
+  const u64 top = wave_top32<NL, true>(k, lane, buf[w]);
   if (lane < 32) lists[w][lane] = top;
   __syncthreads();
   if (w != 0) return;
@@ -281,13 +377,14 @@ __global__ __launch_bounds__(256) void sample_row_kernel(SampleParams p) {
 
 int launch_sample(const SampleParams& p, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(sample_chunk_kernel, dim3(p.chunks, p.M), dim3(256), 0, st, p);
+  if (p.V % 4 == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0)
+    hipLaunchKernelGGL(sample_chunk_kernel<4>, dim3(p.chunks, p.M), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(sample_chunk_kernel<1>, dim3(p.chunks, p.M), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
-  // C * 32 keys per wave, 64 lanes: C / 2 keys per lane
-  if (p.chunks <= 32)
-    hipLaunchKernelGGL(sample_row_kernel<16>, dim3(p.M), dim3(256), 0, st, p);
-  else if (p.chunks <= 64)
+  // C lists per wave: one list (32 keys) per lane up to C = 64, two beyond
+  if (p.chunks <= 64)
     hipLaunchKernelGGL(sample_row_kernel<32>, dim3(p.M), dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL(sample_row_kernel<64>, dim3(p.M), dim3(256), 0, st, p);
