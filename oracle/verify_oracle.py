@@ -37,6 +37,9 @@ Readings where the pages are silent (each is listed in the design doc):
     and never selects NaN; a row with no non-NaN value reports -1.
   * Draft j of a lane is compared with the argmax of verify row j; accept
     length = matched prefix + 1 ([P4] "How DSpark is wired in").
+  * Affine 4-bit: w = scale * q + bias with q the unsigned nibble (0..15),
+    low nibble = even k, scale and bias bf16 per 64 consecutive K; codes
+    [N][K/2], scales and biases [N][K/64] (as bf16 bit patterns).
 """
 from __future__ import annotations
 
@@ -50,6 +53,7 @@ __all__ = [
     "bf16_bits_to_f64", "round_to_bf16_bits",
     "unpack_nibbles", "dequant_nvfp4", "dequant_fp8",
     "gemm_nvfp4", "gemm_fp8", "mlp_silu_mul", "silu",
+    "AFFINE_GROUP", "dequant_affine_q4", "gemm_affine_q4", "mlp_silu_mul_affine",
     "argmax_lowest", "top2_gap", "greedy_accept",
     "bytes_nvfp4", "bytes_fp8", "pass_schedule", "pass_bytes_by_kind",
     "roof_tokens_per_s", "flops_per_byte_nvfp4",
@@ -219,6 +223,55 @@ def gemm_fp8(x_bits: np.ndarray, w: np.ndarray, w_scale: float,
         r1 = min(n, r0 + _ROW_CHUNK)
         y[:, r0:r1] = x @ dequant_fp8(w[r0:r1]).T
     return y * s
+
+
+# ---------------------------------------------------------------------------
+# O11: the affine 4-bit format ([P1] "The engine hard-codes the model": per
+# group of 64 inputs, 32 bytes of nibbles plus a bf16 scale and a bf16 bias,
+# 9 bytes per 16 weights; [P4] "Formats, and what runs where": the affine INT4
+# layout of MLX/AWQ/GPTQ, kept bit-exact; [P2] "What actually moved the
+# needle": the bias term needs per-group sums of the inputs).
+# ---------------------------------------------------------------------------
+
+AFFINE_GROUP = 64
+
+
+def dequant_affine_q4(codes: np.ndarray, scales_bits: np.ndarray, biases_bits: np.ndarray) -> np.ndarray:
+    """W[n,k] = scale[n, k//64] * q[n,k] + bias[n, k//64] in fp64, with q the
+    unsigned nibble 0..15 (low nibble = even k) and scale, bias bf16. Every
+    term is exact in fp64 (bf16 times a 4-bit integer plus bf16)."""
+    q = unpack_nibbles(codes).astype(np.float64)
+    r, k = q.shape
+    sb = np.asarray(scales_bits)
+    bb = np.asarray(biases_bits)
+    assert sb.shape == (r, k // AFFINE_GROUP) and bb.shape == sb.shape, (sb.shape, bb.shape, (r, k))
+    s = np.repeat(bf16_bits_to_f64(sb), AFFINE_GROUP, axis=1)
+    b = np.repeat(bf16_bits_to_f64(bb), AFFINE_GROUP, axis=1)
+    return s * q + b
+
+
+def gemm_affine_q4(x_bits: np.ndarray, codes: np.ndarray, scales_bits: np.ndarray, biases_bits: np.ndarray,
+                   rows: np.ndarray | None = None) -> np.ndarray:
+    """Y[M,N] = X[M,K] . W^T with W dequantised from affine 4-bit, fp64."""
+    x = bf16_bits_to_f64(x_bits)
+    if rows is not None:
+        rows = np.asarray(rows)
+        w = dequant_affine_q4(np.asarray(codes)[rows], np.asarray(scales_bits)[rows], np.asarray(biases_bits)[rows])
+        return x @ w.T
+    n = codes.shape[0]
+    y = np.empty((x.shape[0], n), dtype=np.float64)
+    for r0 in range(0, n, _ROW_CHUNK):
+        r1 = min(n, r0 + _ROW_CHUNK)
+        y[:, r0:r1] = x @ dequant_affine_q4(codes[r0:r1], scales_bits[r0:r1], biases_bits[r0:r1]).T
+    return y
+
+
+def mlp_silu_mul_affine(x_bits, codes, scales_bits, biases_bits, n_inter: int):
+    """silu(gate) * up on a fused [gate; up] affine 4-bit matrix (2*n_inter
+    rows), fp64, and its single bf16 rounding."""
+    gu = gemm_affine_q4(x_bits, codes, scales_bits, biases_bits)
+    h = silu(gu[:, :n_inter]) * gu[:, n_inter:]
+    return h, round_to_bf16_bits(h)
 
 
 def silu(g: np.ndarray) -> np.ndarray:
