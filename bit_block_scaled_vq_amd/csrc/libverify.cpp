@@ -84,6 +84,8 @@ size_t packed_bytes(int32_t kind, int64_t rows, int64_t k) {
   if (kind == VQ_PACK_NVFP4) return (size_t)((rows + 63) / 64 * iters) * vq::kBlockF4;
   if (kind == VQ_PACK_NVFP4_GATE_UP) return rows % 2 ? 0 : (size_t)((rows / 2 + 31) / 32 * iters) * vq::kBlockF4;
   if (kind == VQ_PACK_FP8) return (size_t)((rows + 63) / 64 * iters) * vq::kBlockF8;
+  if (kind == VQ_PACK_AFFINE_Q4) return (size_t)((rows + 63) / 64 * iters) * vq::kBlockF4;
+  if (kind == VQ_PACK_AFFINE_Q4_GATE_UP) return rows % 2 ? 0 : (size_t)((rows / 2 + 31) / 32 * iters) * vq::kBlockF4;
   return 0;
 }
 
@@ -214,6 +216,10 @@ size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K) {
       return vq::make_schedule(vq::EPI_SILU, N, K).bytes;
     case VQ_OP_FP8: return vq::make_schedule(vq::EPI_NONE, N, K).bytes;
     case VQ_OP_LMHEAD: return vq::make_schedule(vq::EPI_ARGMAX, N, K).bytes;
+    case VQ_OP_AFFINE_Q4: return vq::make_schedule(vq::EPI_NONE, N, K).bytes;
+    case VQ_OP_AFFINE_Q4_SILU_MUL:
+      if (N > (1 << 29)) return 0;
+      return vq::make_schedule(vq::EPI_SILU, N, K).bytes;
     default: return 0;
   }
 }
@@ -303,6 +309,70 @@ int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* w, size_t w_bytes, float
   p.y_f32 = y_dtype == VQ_OUT_F32;
   bind_workspace(p, s, workspace);
   return launch(vq::FMT_NVFP4, epi, p, stream);
+}
+
+int32_t vq_pack_affine_q4(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases, int32_t rows,
+                          int32_t K, int32_t gate_up, uint8_t* packed, size_t packed_bytes_avail, void* stream) {
+  if (!codes || !scales || !biases || !packed)
+    return fail(VQ_ERR_NULL, "vq_pack_affine_q4: codes, scales, biases and packed are required");
+  if (gate_up != 0 && gate_up != 1) return fail(VQ_ERR_VALUE, "gate_up must be 0 or 1");
+  const int32_t kind = gate_up ? VQ_PACK_AFFINE_Q4_GATE_UP : VQ_PACK_AFFINE_Q4;
+  if (rows < 1 || rows > (1 << 30) || (gate_up && rows % 2)) return fail(VQ_ERR_SHAPE, "rows = %d invalid", rows);
+  if (K < vq::kIterK || K % vq::kIterK != 0 || K > (1 << 24))
+    return fail(VQ_ERR_SHAPE, "K = %d must be a positive multiple of %d (at most 2^24)", K, vq::kIterK);
+  if (!aligned(codes, 16) || !aligned(scales, 16) || !aligned(biases, 16) || !aligned(packed, 16))
+    return fail(VQ_ERR_ALIGN, "codes, scales, biases and packed must be 16-byte aligned");
+  const size_t need = packed_bytes(kind, rows, K);
+  if (packed_bytes_avail < need) return fail(VQ_ERR_SHAPE, "packed buffer has %zu bytes, %zu needed", packed_bytes_avail, need);
+  int32_t st = check_device();
+  if (st) return st;
+  vq::PackParams p{};
+  p.codes = codes;
+  p.scales = reinterpret_cast<const uint8_t*>(scales);
+  p.biases = reinterpret_cast<const uint8_t*>(biases);
+  p.out = packed;
+  p.rows = rows;
+  p.K = K;
+  p.gate_up = gate_up;
+  p.tiles = gate_up ? (rows / 2 + 31) / 32 : (rows + 63) / 64;
+  p.iters = K / vq::kIterK;
+  const int err = vq::launch_pack(vq::FMT_AFFINE, p, stream);
+  if (err) return fail(VQ_ERR_LAUNCH, "pack launch failed: %s", hipGetErrorString((hipError_t)err));
+  return VQ_OK;
+}
+
+int32_t vq_gemm_affine_q4(const uint16_t* x, const uint8_t* w, size_t w_bytes, void* y, int32_t y_dtype, int32_t M,
+                          int32_t N, int32_t K, int32_t epilogue, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!x || !w || !y) return fail(VQ_ERR_NULL, "vq_gemm_affine_q4: x, w and y are required");
+  if (y_dtype != VQ_OUT_BF16 && y_dtype != VQ_OUT_F32) return fail(VQ_ERR_VALUE, "unknown y_dtype %d", y_dtype);
+  if (epilogue != VQ_EPI_NONE && epilogue != VQ_EPI_SILU_MUL) return fail(VQ_ERR_VALUE, "unknown epilogue %d", epilogue);
+  int32_t st = check_shape(M, N, K);
+  if (st) return st;
+  if (epilogue == VQ_EPI_SILU_MUL && N > (1 << 29)) return fail(VQ_ERR_SHAPE, "N = %d too large for SILU_MUL", N);
+  if (!aligned(x, 16)) return fail(VQ_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(y, y_dtype == VQ_OUT_F32 ? 4 : 2)) return fail(VQ_ERR_ALIGN, "y is not aligned to its element size");
+  const bool silu = epilogue == VQ_EPI_SILU_MUL;
+  st = check_w(w, w_bytes, silu ? packed_bytes(VQ_PACK_AFFINE_Q4_GATE_UP, 2 * (int64_t)N, K)
+                                 : packed_bytes(VQ_PACK_AFFINE_Q4, N, K));
+  if (st) return st;
+  const int epi = silu ? vq::EPI_SILU : vq::EPI_NONE;
+  const vq::Schedule s = vq::make_schedule(epi, N, K);
+  st = check_ws(s, workspace, workspace_bytes);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  vq::GemmParams p{};
+  p.x = x;
+  p.w = w;
+  p.out_scale = 1.0f;
+  p.y = y;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.y_f32 = y_dtype == VQ_OUT_F32;
+  bind_workspace(p, s, workspace);
+  return launch(vq::FMT_AFFINE, epi, p, stream);
 }
 
 int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, size_t w_bytes, float w_scale, void* y, int32_t y_dtype,

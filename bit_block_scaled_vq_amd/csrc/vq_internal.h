@@ -10,7 +10,10 @@ namespace vq {
 // scale blocks per MFMA through zero-padded activation rows; up to 8 rows per
 // row group). FMT_NVFP4S: the same packed weights scaled in registers before
 // the MFMA (exact in bf16), 16 activation rows per row group.
-enum Fmt : int { FMT_NVFP4 = 0, FMT_FP8 = 1, FMT_NVFP4S = 2 };
+// FMT_AFFINE: affine 4-bit, w = scale * q + bias per group of 64 K (bf16 scale
+// and bias), 16 activation rows per row group; the packed block has the NVFP4
+// code layout and 512 B of (scale, bias) pairs.
+enum Fmt : int { FMT_NVFP4 = 0, FMT_FP8 = 1, FMT_NVFP4S = 2, FMT_AFFINE = 3 };
 enum Epi : int { EPI_NONE = 0, EPI_SILU = 1, EPI_ARGMAX = 2 };
 
 // Packed weights are laid out in blocks of one tile (64 weight rows, four
@@ -77,7 +80,8 @@ struct GemmParams {
 
 struct PackParams {
   const uint8_t* codes;   // NVFP4 codes [rows][K/2] or FP8 weights [rows][K]
-  const uint8_t* scales;  // NVFP4 scales [rows][K/16]
+  const uint8_t* scales;  // NVFP4 scales [rows][K/16]; affine: bf16 scales [rows][K/64]
+  const uint8_t* biases;  // affine: bf16 biases [rows][K/64]
   uint8_t* out;
   int32_t rows, K;        // rows of the canonical matrix
   int32_t gate_up;        // NVFP4: tiles pair gate row r with up row r + rows/2

@@ -90,6 +90,21 @@ __device__ __forceinline__ bf16x8_t dec_fp4x8_scaled(uint32_t w, float sc) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
+// 8 unsigned 4-bit codes (one dword, low nibble first) -> their values 0..15
+// as 8 bf16 in k order (exact).
+__device__ __forceinline__ bf16x8_t dec_q4x8(uint32_t w) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  u32x4_t r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x2_t v = {(float)((lo >> (8 * b)) & 0xFFu), (float)((hi >> (8 * b)) & 0xFFu)};
+    r[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  }
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
 // 8 E4M3FN codes (two dwords, byte order = k order) -> 8 bf16.
 __device__ __forceinline__ bf16x8_t dec_fp8x8(uint32_t lo, uint32_t hi) {
   auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -187,6 +202,46 @@ __global__ __launch_bounds__(256) void pack_nvfp4_kernel(PackParams p) {
     pack_nvfp4_chunk(p, gid);
 }
 
+// One thread per 16-byte chunk of a packed affine block (288 chunks): the 256
+// code chunks as for NVFP4, then 32 chunks of (scale, bias) pairs. Chunk
+// (n, part) holds, for sub-tiles t = 2 part, 2 part + 1 of row n and groups
+// h = 0, 1 of the iteration, the bf16 pairs (scale, bias) as two 16-bit
+// halves of one dword: t, then h.
+__device__ __forceinline__ void pack_affine_chunk(const PackParams& p, int64_t gid) {
+  const int64_t blk = gid / 288;
+  const int c = (int)(gid - blk * 288);
+  if (c < 256) {
+    pack_nvfp4_chunk(p, gid);
+    return;
+  }
+  const int tile = (int)(blk / p.iters), it = (int)(blk - (int64_t)tile * p.iters);
+  const size_t G = (size_t)p.K / 64;
+  const int n = (c - 256) >> 1, part = (c - 256) & 1;
+  uint32_t words[4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int r = pack_row(p, tile, 2 * part + tt, n);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t wv = 0u;
+      if (r >= 0) {
+        const size_t gi = (size_t)r * G + (size_t)it * 2 + h;
+        wv = (uint32_t)reinterpret_cast<const uint16_t*>(p.scales)[gi] |
+             ((uint32_t)reinterpret_cast<const uint16_t*>(p.biases)[gi] << 16);
+      }
+      words[2 * tt + h] = wv;
+    }
+  }
+  *reinterpret_cast<u32x4_t*>(p.out + blk * kBlockF4 + (size_t)c * 16) = u32x4_t{words[0], words[1], words[2], words[3]};
+}
+
+__global__ __launch_bounds__(256) void pack_affine_kernel(PackParams p) {
+  const int64_t nchunks = (int64_t)p.tiles * p.iters * 288;
+  for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < nchunks;
+       gid += (int64_t)gridDim.x * blockDim.x)
+    pack_affine_chunk(p, gid);
+}
+
 // One thread per 16-byte chunk of a packed FP8 block (512 chunks). Chunk
 // (t, h, l): lane l = 16g + n gets the 8 weights of k [128*it + 32j + 8g, +8)
 // for j = 2h and j = 2h+1 of row (t, n).
@@ -248,6 +303,11 @@ struct WBuf<FMT_NVFP4> {
 template <>
 struct WBuf<FMT_NVFP4S> : WBuf<FMT_NVFP4> {};
 template <>
+struct WBuf<FMT_AFFINE> {
+  u32x4_t c[kNT];   // per sub-tile: code dwords of MFMA steps 0..3
+  u32x4_t sb[2];    // (scale, bias) of this lane's row: sub-tiles 0,1 then 2,3; groups 0,1
+};
+template <>
 struct WBuf<FMT_FP8> {
   u32x4_t c[kNT][2];  // per sub-tile: weights of MFMA steps (0,1) and (2,3)
 };
@@ -258,7 +318,12 @@ struct XBuf {
 
 template <int FMT>
 __device__ __forceinline__ void load_w(WBuf<FMT>& b, const uint8_t* blk, int lane) {
-  if constexpr (FMT != FMT_FP8) {
+  if constexpr (FMT == FMT_AFFINE) {
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) b.c[t] = ld16(blk + t * 1024 + lane * 16);
+    b.sb[0] = ld16(blk + 4096 + (lane & 15) * 32);
+    b.sb[1] = ld16(blk + 4096 + (lane & 15) * 32 + 16);
+  } else if constexpr (FMT != FMT_FP8) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) b.c[t] = ld16(blk + t * 1024 + lane * 16);
     b.s = ld16(blk + 4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
@@ -352,6 +417,43 @@ __device__ __forceinline__ void compute_iter(const WBuf<FMT>& b, const XBuf<RG>&
           a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[rg][j]), wv, a, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc.v[t][4 * rg + r] = a[r];
+        }
+      }
+    }
+  } else if constexpr (FMT == FMT_AFFINE) {
+    // sum_k x (s q + b) over a group of 64 = s * (x . q) + b * (sum of x):
+    // per group and sub-tile two MFMAs give x . q for the lane's row; the
+    // group sums of x come from two MFMAs against ones (shared by the
+    // sub-tiles), in the same accumulator layout.
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    f32x4_t sx[RG][2];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        sx[rg][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[rg][2 * h]), ones,
+                                                            f32x4_t{}, 0, 0, 0);
+        sx[rg][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[rg][2 * h + 1]), ones,
+                                                            sx[rg][h], 0, 0, 0);
+      }
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8_t w0 = dec_q4x8(b.c[t][2 * h]);
+        const bf16x8_t w1 = dec_q4x8(b.c[t][2 * h + 1]);
+        const uint32_t pair = b.sb[t >> 1][2 * (t & 1) + h];
+        const float sc = __uint_as_float(pair << 16);
+        const float bi = __uint_as_float(pair & 0xFFFF0000u);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[rg][2 * h]), w0,
+                                                              f32x4_t{}, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[rg][2 * h + 1]), w1, d, 0,
+                                                      0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc.v[t][4 * rg + r] = __builtin_fmaf(sc, d[r], __builtin_fmaf(bi, sx[rg][h][r], acc.v[t][4 * rg + r]));
         }
       }
     }
@@ -821,16 +923,21 @@ int launch_gemm(int fmt, int epi, const GemmParams& p, void* stream) {
     if (epi == EPI_SILU) return launch_rg<FMT_NVFP4, EPI_SILU>(p, st);
     return launch_rg<FMT_NVFP4, EPI_ARGMAX>(p, st);
   }
+  if (fmt == FMT_AFFINE) {
+    if (epi == EPI_SILU) return launch_rg<FMT_AFFINE, EPI_SILU>(p, st);
+    return launch_rg<FMT_AFFINE, EPI_NONE>(p, st);
+  }
   return launch_rg<FMT_FP8, EPI_NONE>(p, st);
 }
 
 int launch_pack(int fmt, const PackParams& p, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int64_t chunks = (int64_t)p.tiles * p.iters * (fmt == FMT_NVFP4 ? 288 : 512);
+  const int64_t chunks = (int64_t)p.tiles * p.iters * (fmt == FMT_FP8 ? 512 : 288);
   int64_t groups = (chunks + 255) / 256;
   if (groups > 65536) groups = 65536;  // grid-stride beyond this
   const dim3 grid((unsigned)groups), block(256);
   if (fmt == FMT_NVFP4) hipLaunchKernelGGL(pack_nvfp4_kernel, grid, block, 0, st, p);
+  else if (fmt == FMT_AFFINE) hipLaunchKernelGGL(pack_affine_kernel, grid, block, 0, st, p);
   else hipLaunchKernelGGL(pack_fp8_kernel, grid, block, 0, st, p);
   return (int)hipGetLastError();
 }

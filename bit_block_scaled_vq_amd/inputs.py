@@ -41,6 +41,7 @@ T_DRAFT = 4
 T_LOGITS = 5
 T_UNIFORM = 6
 T_DRAFT_Q = 7
+T_AFFINE = 8
 
 LOGIT_STD = 2.5
 
@@ -134,6 +135,28 @@ def drafts(key, argmax_rows: np.ndarray, vocab: int, p: float = DRAFT_P) -> np.n
     return np.where(u < p, a[:, : r - 1], rand_ids).astype(np.int32)
 
 
+def affine_weights(key, n: int, k: int):
+    """Affine 4-bit matrix [n][k]: (codes uint8 [n][k/2], scales and biases as
+    bf16 bit patterns uint16 [n][k/64])."""
+    codes = np.empty((n, k // 2), dtype=np.uint8)
+    sb = np.empty((n, k // 64), dtype=np.uint16)
+    bb = np.empty((n, k // 64), dtype=np.uint16)
+    chunks = [(c, r0, min(n, r0 + CHUNK_ROWS)) for c, r0 in enumerate(range(0, n, CHUNK_ROWS))]
+
+    def work(item):
+        c, r0, r1 = item
+        g = rng(*key, T_AFFINE, c)
+        codes[r0:r1] = g.integers(0, 256, size=(r1 - r0, k // 2), dtype=np.uint8)
+        s = np.abs(g.standard_normal((r1 - r0, k // 64), dtype=np.float32)) * np.float32(0.004) + np.float32(0.001)
+        b = np.float32(-7.5) * s * (np.float32(1) + g.standard_normal((r1 - r0, k // 64), dtype=np.float32) / 5)
+        sb[r0:r1] = to_bf16_bits(s)
+        bb[r0:r1] = to_bf16_bits(b)
+
+    with _cf.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(work, chunks))
+    return codes, sb, bb
+
+
 def logits_f32(key, m: int, v: int, std: float = LOGIT_STD) -> np.ndarray:
     """Verify logits [m][v] (float32), N(0, std^2)."""
     return (rng(*key, T_LOGITS).standard_normal((m, v), dtype=np.float32) * np.float32(std)).astype(np.float32)
@@ -203,6 +226,16 @@ def device_fp8_weights(key, n: int, k: int, device, std: float = FP8_STD):
         w = torch.randn((r1 - r0, k), generator=g, device=device, dtype=torch.float32).mul_(std)
         out[r0:r1] = w.to(torch.float8_e4m3fn).view(torch.uint8)
     return out
+
+
+def device_affine_weights(key, n: int, k: int, device):
+    """Same distributions as affine_weights, drawn on the device."""
+    torch = _torch()
+    g = _torch_gen(device, *key, T_AFFINE)
+    codes = torch.randint(0, 256, (n, k // 2), generator=g, device=device, dtype=torch.uint8)
+    s = torch.randn((n, k // 64), generator=g, device=device, dtype=torch.float32).abs_().mul_(0.004).add_(0.001)
+    b = torch.randn((n, k // 64), generator=g, device=device, dtype=torch.float32).div_(5).add_(1).mul_(s).mul_(-7.5)
+    return codes, s.to(torch.bfloat16).view(torch.int16), b.to(torch.bfloat16).view(torch.int16)
 
 
 def device_drafts(key, argmax_rows, vocab: int, p: float = DRAFT_P):

@@ -32,12 +32,16 @@ VQ_OP_NVFP4_SILU_MUL = 1
 VQ_OP_FP8 = 2
 VQ_OP_LMHEAD = 3
 VQ_OP_SAMPLE = 4
+VQ_OP_AFFINE_Q4 = 5
+VQ_OP_AFFINE_Q4_SILU_MUL = 6
 VQ_PACK_NVFP4 = 0
 VQ_PACK_NVFP4_GATE_UP = 1
 VQ_PACK_FP8 = 2
+VQ_PACK_AFFINE_Q4 = 3
+VQ_PACK_AFFINE_Q4_GATE_UP = 4
 
 EXPORTS = [
-    "vq_packed_bytes", "vq_pack_nvfp4", "vq_pack_fp8",
+    "vq_packed_bytes", "vq_pack_nvfp4", "vq_pack_fp8", "vq_pack_affine_q4", "vq_gemm_affine_q4",
     "vq_gemm_nvfp4", "vq_gemm_fp8", "vq_lmhead_argmax_accept", "vq_sample_accept", "vq_workspace_bytes",
     "vq_status_str", "vq_last_error", "vq_abi_version", "vq_probe_copy", "vq_probe_read",
 ]
@@ -69,6 +73,10 @@ def lib() -> ctypes.CDLL:
     L.vq_pack_fp8.restype = i32
     L.vq_gemm_nvfp4.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, i32, i32, vp, sz, vp]
     L.vq_gemm_nvfp4.restype = i32
+    L.vq_pack_affine_q4.argtypes = [vp, vp, vp, i32, i32, i32, vp, sz, vp]
+    L.vq_pack_affine_q4.restype = i32
+    L.vq_gemm_affine_q4.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.vq_gemm_affine_q4.restype = i32
     L.vq_gemm_fp8.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, i32, vp, sz, vp]
     L.vq_gemm_fp8.restype = i32
     L.vq_lmhead_argmax_accept.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, i32,
@@ -186,6 +194,44 @@ def pack_fp8(w, stream=None):
     out = torch.empty(n, dtype=torch.uint8, device=w.device)
     _check(lib().vq_pack_fp8(_ptr(w), rows, K, _ptr(out), n, _stream(stream)))
     return out
+
+
+def pack_affine_q4(codes, scales, biases, gate_up: bool = False, stream=None):
+    """Packed form (1-D uint8 device tensor) of an affine 4-bit matrix: codes
+    uint8 [rows][K/2], scales and biases bf16 (or their int16 bit patterns)
+    [rows][K/64]; gate_up packs a fused [gate; up] matrix for VQ_EPI_SILU_MUL."""
+    torch = _torch()
+    _need(codes, "codes", (torch.uint8,), 2)
+    _need(scales, "scales", (torch.bfloat16, torch.int16), 2)
+    _need(biases, "biases", (torch.bfloat16, torch.int16), 2)
+    rows, K = codes.shape[0], 2 * codes.shape[1]
+    if tuple(scales.shape) != (rows, K // 64) or tuple(biases.shape) != (rows, K // 64):
+        raise ValueError(f"shape mismatch: codes {tuple(codes.shape)} scales {tuple(scales.shape)} "
+                         f"biases {tuple(biases.shape)}")
+    n = packed_bytes(VQ_PACK_AFFINE_Q4_GATE_UP if gate_up else VQ_PACK_AFFINE_Q4, rows, K)
+    if n == 0:
+        raise VerifyError(VQ_ERR_SHAPE, f"invalid shape for packing: rows={rows} K={K}")
+    out = torch.empty(n, dtype=torch.uint8, device=codes.device)
+    _check(lib().vq_pack_affine_q4(_ptr(codes), _ptr(scales), _ptr(biases), rows, K, int(bool(gate_up)), _ptr(out),
+                                   n, _stream(stream)))
+    return out
+
+
+def vq_gemm_affine_q4(x, w, y, epilogue: int = VQ_EPI_NONE, workspace=None, stream=None):
+    """y[M][N] = x . W^T (affine 4-bit W, packed by pack_affine_q4), or
+    silu(gate)*up for VQ_EPI_SILU_MUL (w packed with gate_up=True)."""
+    torch = _torch()
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(w, "w", (torch.uint8,), 1)
+    _need(y, "y", (torch.bfloat16, torch.float32), 2)
+    M, K = x.shape
+    N = y.shape[1]
+    if y.shape[0] != M:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)} y {tuple(y.shape)}")
+    ws_ptr, ws_n = _ws(workspace)
+    _check(lib().vq_gemm_affine_q4(_ptr(x), _ptr(w), w.numel(), _ptr(y), _out_dtype(y), M, N, K, int(epilogue),
+                                   ws_ptr, ws_n, _stream(stream)))
+    return y
 
 
 def _ws(workspace):

@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define VQ_ABI_VERSION 3
+#define VQ_ABI_VERSION 4
 
 typedef enum {
   VQ_OK = 0,
@@ -96,8 +96,14 @@ typedef enum {
 
 typedef enum { VQ_OUT_BF16 = 0, VQ_OUT_F32 = 1 } vq_out_dtype;
 typedef enum { VQ_EPI_NONE = 0, VQ_EPI_SILU_MUL = 1 } vq_epilogue;
-typedef enum { VQ_OP_NVFP4 = 0, VQ_OP_NVFP4_SILU_MUL = 1, VQ_OP_FP8 = 2, VQ_OP_LMHEAD = 3, VQ_OP_SAMPLE = 4 } vq_op;
-typedef enum { VQ_PACK_NVFP4 = 0, VQ_PACK_NVFP4_GATE_UP = 1, VQ_PACK_FP8 = 2 } vq_pack_kind;
+typedef enum {
+  VQ_OP_NVFP4 = 0, VQ_OP_NVFP4_SILU_MUL = 1, VQ_OP_FP8 = 2, VQ_OP_LMHEAD = 3, VQ_OP_SAMPLE = 4,
+  VQ_OP_AFFINE_Q4 = 5, VQ_OP_AFFINE_Q4_SILU_MUL = 6
+} vq_op;
+typedef enum {
+  VQ_PACK_NVFP4 = 0, VQ_PACK_NVFP4_GATE_UP = 1, VQ_PACK_FP8 = 2,
+  VQ_PACK_AFFINE_Q4 = 3, VQ_PACK_AFFINE_Q4_GATE_UP = 4
+} vq_pack_kind;
 
 /* Bytes of the packed form of a canonical matrix of `rows` rows and K columns
  * (VQ_PACK_NVFP4_GATE_UP: the fused [gate; up] matrix, rows = 2N, even).
@@ -135,6 +141,34 @@ int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* w, size_t w_bytes,
                       float tensor_scale, void* y, int32_t y_dtype,
                       int32_t M, int32_t N, int32_t K, int32_t epilogue,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Affine 4-bit weights ("144 tok/s needs 502 GB/s ...", section "The engine
+ * hard-codes the model": per group of 64 inputs, 32 bytes of nibbles plus a
+ * bf16 scale and a bf16 bias, 9 bytes per 16 weights; "lithos-metal ...",
+ * section "Formats, and what runs where": the MLX/AWQ/GPTQ affine INT4
+ * layout):  W[n][k] = scale[n][k/64] * q[n][k] + bias[n][k/64], q the unsigned
+ * nibble 0..15.
+ * Canonical layout: codes uint8 [rows][K/2] (low nibble = even k, as for
+ * NVFP4); scales and biases bf16 bit patterns uint16 [rows][K/64].
+ * Packed layout: the NVFP4 block (4608 B per 64 rows x 128 K) with the same
+ * 4096 B of codes, then for row n of the tile the 32 bytes at 4096 + 32n:
+ * for sub-tile t = 0..3 and group h = 0, 1 of the iteration one dword
+ * holding scale (low half) and bias (high half). gate_up = 1 pairs gate and
+ * up rows exactly as vq_pack_nvfp4 does. */
+int32_t vq_pack_affine_q4(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases,
+                          int32_t rows, int32_t K, int32_t gate_up, uint8_t* packed,
+                          size_t packed_bytes, void* stream);
+
+/* Affine 4-bit skinny GEMM: Y[M][N] = X . W^T, with epilogue VQ_EPI_NONE or
+ * VQ_EPI_SILU_MUL (w from vq_pack_affine_q4 with gate_up = 0 / 1, as for
+ * vq_gemm_nvfp4). The bias term uses the per-group sums of X, formed by the
+ * matrix unit next to the products ("Beating Splash on an M5 Max ...",
+ * section "What actually moved the needle": the Q4 tiles need per-group
+ * input sums). y [M][N] bf16 or fp32. Workspace:
+ * vq_workspace_bytes(VQ_OP_AFFINE_Q4[_SILU_MUL], M, N, K). */
+int32_t vq_gemm_affine_q4(const uint16_t* x, const uint8_t* w, size_t w_bytes, void* y,
+                          int32_t y_dtype, int32_t M, int32_t N, int32_t K, int32_t epilogue,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* FP8 skinny GEMM: Y[M][N] = (X[M][K] . E4M3(w)^T) * w_scale
  * ("lithos-metal ...", section "What one token costs the bus": every Gated

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = ops.lib()
-    assert L.vq_abi_version() == 3
+    assert L.vq_abi_version() == 4
     assert ops.status_str(ops.VQ_OK) == "VQ_OK"
     assert ops.status_str(ops.VQ_ERR_WORKSPACE) == "VQ_ERR_WORKSPACE"
     assert ops.status_str(99) == "VQ_ERR_UNKNOWN"
@@ -166,6 +166,31 @@ def test_packed_bytes():
     # the model's matrices pack without padding (row counts are multiples of 64)
     assert L.vq_packed_bytes(ops.VQ_PACK_NVFP4_GATE_UP, 2 * 17408, 5120) == 2 * 17408 * 5120 * 9 // 16
     assert L.vq_packed_bytes(ops.VQ_PACK_NVFP4, 248320, 5120) == 248320 * 5120 * 9 // 16
+
+
+def test_affine_validation():
+    L = ops.lib()
+    n = 1 << 30
+    assert L.vq_pack_affine_q4(A, A, None, 64, 128, 0, A, n, None) == ops.VQ_ERR_NULL
+    assert L.vq_pack_affine_q4(A, A, A, 64, 128, 2, A, n, None) == ops.VQ_ERR_VALUE
+    assert L.vq_pack_affine_q4(A, A, A, 63, 128, 1, A, n, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_pack_affine_q4(A, A, A, 64, 64, 0, A, n, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_pack_affine_q4(A, A, A + 2, 64, 128, 0, A, n, None) == ops.VQ_ERR_ALIGN
+    assert L.vq_pack_affine_q4(A, A, A, 64, 128, 0, A, 4607, None) == ops.VQ_ERR_SHAPE
+    g = L.vq_gemm_affine_q4
+    assert g(None, A, n, A, 0, 8, 64, 128, 0, A, n, None) == ops.VQ_ERR_NULL
+    assert g(A, A, n, A, 3, 8, 64, 128, 0, A, n, None) == ops.VQ_ERR_VALUE
+    assert g(A, A, n, A, 0, 8, 64, 128, 2, A, n, None) == ops.VQ_ERR_VALUE
+    assert g(A, A, n, A, 0, 33, 64, 128, 0, A, n, None) == ops.VQ_ERR_SHAPE
+    assert g(A, A, n, A, 0, 8, 64, 192, 0, A, n, None) == ops.VQ_ERR_SHAPE
+    assert g(A, A, 4607, A, 0, 8, 64, 128, 0, A, n, None) == ops.VQ_ERR_SHAPE
+    assert g(A, A, n, A, 0, 8, 64, 128, 0, A, 8, None) == ops.VQ_ERR_WORKSPACE
+    # same packed sizes as NVFP4: 9 bytes per 16 weights
+    for rows, k in ((64, 128), (130, 512), (2 * 17408, 5120)):
+        assert L.vq_packed_bytes(ops.VQ_PACK_AFFINE_Q4, rows, k) == L.vq_packed_bytes(ops.VQ_PACK_NVFP4, rows, k)
+        assert L.vq_packed_bytes(ops.VQ_PACK_AFFINE_Q4_GATE_UP, rows, k) == \
+            L.vq_packed_bytes(ops.VQ_PACK_NVFP4_GATE_UP, rows, k)
+    assert L.vq_workspace_bytes(ops.VQ_OP_AFFINE_Q4, 8, 5120, 17408) == L.vq_workspace_bytes(ops.VQ_OP_NVFP4, 8, 5120, 17408)
 
 
 def test_pack_validation():
