@@ -238,6 +238,49 @@ def m_sweep(torch, ops, inputs_mod, p, rows=(1, 8, 16, 24, 32), reps=2):
     return out
 
 
+def affine_q4(torch, ops, inputs_mod, dev, layers=4, rows=(8, 32), reps=3):
+    """The MLP in the affine 4-bit format (scale and bias per 64, the same 9
+    bytes per 16 weights as NVFP4): weight GB/s per launch of [gate; up] +
+    SiLU*up and of down, rotating over `layers` layers' seeded weights (more
+    than the 256 MB MALL holds)."""
+    gu, dn = [], []
+    for l in range(layers):
+        c, s, b = inputs_mod.device_affine_weights((5, 5000, l, 0), 2 * INTER, HIDDEN, dev)
+        gu.append(ops.pack_affine_q4(c, s, b, gate_up=True))
+        c, s, b = inputs_mod.device_affine_weights((5, 5000, l, 1), HIDDEN, INTER, dev)
+        dn.append(ops.pack_affine_q4(c, s, b))
+        del c, s, b
+    out = {}
+    for m in rows:
+        x = inputs_mod.device_x_bf16((5, 5001, m), m, HIDDEN, dev)
+        h = inputs_mod.device_x_bf16((5, 5002, m), m, INTER, dev)
+        hy = torch.empty((m, INTER), dtype=torch.bfloat16, device=dev)
+        yy = torch.empty((m, HIDDEN), dtype=torch.bfloat16, device=dev)
+        ws_gu = ops.workspace(ops.VQ_OP_AFFINE_Q4_SILU_MUL, m, INTER, HIDDEN, dev)
+        ws_dn = ops.workspace(ops.VQ_OP_AFFINE_Q4, m, HIDDEN, INTER, dev)
+        res = {}
+        for kind, run, nbytes in (
+                ("mlp_gate_up", lambda w: ops.vq_gemm_affine_q4(x, w, hy, epilogue=ops.VQ_EPI_SILU_MUL,
+                                                                 workspace=ws_gu), nvfp4_bytes(2 * INTER, HIDDEN)),
+                ("mlp_down", lambda w: ops.vq_gemm_affine_q4(h, w, yy, workspace=ws_dn), nvfp4_bytes(HIDDEN, INTER))):
+            ws_list = gu if kind == "mlp_gate_up" else dn
+            for w in ws_list[:2]:
+                run(w)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                for w in ws_list:
+                    run(w)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * len(ws_list))
+            res[kind] = {"avg_us": round(us, 2), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        out[str(m)] = res
+    del gu, dn
+    torch.cuda.empty_cache()
+    return out
+
+
 def sampled_verify(torch, ops, inputs_mod, p, g_steps=10, reps=20):
     """The end of the pass at nonzero temperature (temperature 1, top_k 32,
     top_p 0.95): the head also writes fp32 logits and vq_sample_accept reads
@@ -501,6 +544,8 @@ def main():
     dom_s = dominant_kernel_duration(torch, p)
     sweep = m_sweep(torch, ops, inputs, p)
     sampled = sampled_verify(torch, ops, inputs, p)
+    affine = affine_q4(torch, ops, inputs, dev)
+    log(f"affine 4-bit MLP at M=8: {affine['8']}")
     log(f"sampled verify: pass {sampled['ms_per_pass_sampled']:.3f} ms, sampler {sampled['sampler_us']:.1f} us")
     gu_w = weight_bytes("nvfp4_silu", INTER, HIDDEN)
     gu_a = act_bytes(INTER, HIDDEN)
@@ -542,6 +587,7 @@ def main():
         "kernels": kinds,
         "m_sweep_weight_gbps": sweep,
         "sampled_verify": sampled,
+        "affine_q4_mlp": affine,
         "roofline": {
             "kernel": "vq_gemm_kernel<NVFP4, SILU_MUL, M<=8> ([gate;up] 34816x5120 + SiLU*up)",
             "bound": "hbm",

@@ -90,18 +90,14 @@ __device__ __forceinline__ bf16x8_t dec_fp4x8_scaled(uint32_t w, float sc) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
-// 8 unsigned 4-bit codes (one dword, low nibble first) -> their values 0..15
-// as 8 bf16 in k order (exact).
-__device__ __forceinline__ bf16x8_t dec_q4x8(uint32_t w) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+// 8 unsigned 4-bit codes in the packed affine order (the even-k nibbles in
+// bits 0-15, the odd-k nibbles in bits 16-31, k ascending within each half)
+// -> 8 bf16 holding 128 + q in k order. bf16 0x43nn is 128 + nn exactly for
+// nn < 128, so each output dword is one mask-and-or of a shifted word.
+__device__ __forceinline__ bf16x8_t dec_q4x8_offset(uint32_t w) {
   u32x4_t r;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const f32x2_t v = {(float)((lo >> (8 * b)) & 0xFFu), (float)((hi >> (8 * b)) & 0xFFu)};
-    r[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-  }
+  for (int b = 0; b < 4; ++b) r[b] = ((w >> (4 * b)) & 0x000F000Fu) | 0x43004300u;
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
@@ -202,19 +198,40 @@ __global__ __launch_bounds__(256) void pack_nvfp4_kernel(PackParams p) {
     pack_nvfp4_chunk(p, gid);
 }
 
+// Canonical code dword (byte j = k 2j low nibble, k 2j+1 high nibble) -> the
+// packed affine order: even-k nibbles in bits 0-15, odd-k nibbles in 16-31.
+__device__ __forceinline__ uint32_t affine_nibble_order(uint32_t w) {
+  auto squeeze = [](uint32_t x) {  // low nibbles of the 4 bytes -> bits 0-15
+    x = (x | (x >> 4)) & 0x00FF00FFu;
+    return (x | (x >> 8)) & 0x0000FFFFu;
+  };
+  return squeeze(w & 0x0F0F0F0Fu) | (squeeze((w >> 4) & 0x0F0F0F0Fu) << 16);
+}
+
 // One thread per 16-byte chunk of a packed affine block (288 chunks): the 256
-// code chunks as for NVFP4, then 32 chunks of (scale, bias) pairs. Chunk
+// code chunks as for NVFP4 (each dword in the affine nibble order), then 32
+// chunks of (scale, bias) pairs. Chunk
 // (n, part) holds, for sub-tiles t = 2 part, 2 part + 1 of row n and groups
 // h = 0, 1 of the iteration, the bf16 pairs (scale, bias) as two 16-bit
 // halves of one dword: t, then h.
 __device__ __forceinline__ void pack_affine_chunk(const PackParams& p, int64_t gid) {
   const int64_t blk = gid / 288;
   const int c = (int)(gid - blk * 288);
+  const int tile = (int)(blk / p.iters), it = (int)(blk - (int64_t)tile * p.iters);
   if (c < 256) {
-    pack_nvfp4_chunk(p, gid);
+    const int t = c >> 6, l = c & 63, n = l & 15, g = l >> 4;
+    const int r = pack_row(p, tile, t, n);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r >= 0) {
+      const uint8_t* row = p.codes + (size_t)r * ((size_t)p.K / 2) + (size_t)it * 64 + g * 4;
+      v.x = affine_nibble_order(*reinterpret_cast<const uint32_t*>(row));
+      v.y = affine_nibble_order(*reinterpret_cast<const uint32_t*>(row + 16));
+      v.z = affine_nibble_order(*reinterpret_cast<const uint32_t*>(row + 32));
+      v.w = affine_nibble_order(*reinterpret_cast<const uint32_t*>(row + 48));
+    }
+    *reinterpret_cast<u32x4_t*>(p.out + blk * kBlockF4 + (size_t)c * 16) = v;
     return;
   }
-  const int tile = (int)(blk / p.iters), it = (int)(blk - (int64_t)tile * p.iters);
   const size_t G = (size_t)p.K / 64;
   const int n = (c - 256) >> 1, part = (c - 256) & 1;
   uint32_t words[4];
@@ -421,10 +438,11 @@ __device__ __forceinline__ void compute_iter(const WBuf<FMT>& b, const XBuf<RG>&
       }
     }
   } else if constexpr (FMT == FMT_AFFINE) {
-    // sum_k x (s q + b) over a group of 64 = s * (x . q) + b * (sum of x):
-    // per group and sub-tile two MFMAs give x . q for the lane's row; the
-    // group sums of x come from two MFMAs against ones (shared by the
-    // sub-tiles), in the same accumulator layout.
+    // sum_k x (s q + b) over a group of 64 = s * (x . (128 + q)) +
+    // (b - 128 s) * (sum of x): per group and sub-tile two MFMAs give
+    // x . (128 + q) for the lane's row; the group sums of x come from two
+    // MFMAs against ones (shared by the sub-tiles), in the same accumulator
+    // layout.
     const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     f32x4_t sx[RG][2];
 #pragma unroll
@@ -440,11 +458,11 @@ __device__ __forceinline__ void compute_iter(const WBuf<FMT>& b, const XBuf<RG>&
     for (int t = 0; t < kNT; ++t) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const bf16x8_t w0 = dec_q4x8(b.c[t][2 * h]);
-        const bf16x8_t w1 = dec_q4x8(b.c[t][2 * h + 1]);
+        const bf16x8_t w0 = dec_q4x8_offset(b.c[t][2 * h]);
+        const bf16x8_t w1 = dec_q4x8_offset(b.c[t][2 * h + 1]);
         const uint32_t pair = b.sb[t >> 1][2 * (t & 1) + h];
         const float sc = __uint_as_float(pair << 16);
-        const float bi = __uint_as_float(pair & 0xFFFF0000u);
+        const float bi = __builtin_fmaf(-128.0f, sc, __uint_as_float(pair & 0xFFFF0000u));
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
           f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[rg][2 * h]), w0,

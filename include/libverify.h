@@ -151,7 +151,9 @@ int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* w, size_t w_bytes,
  * Canonical layout: codes uint8 [rows][K/2] (low nibble = even k, as for
  * NVFP4); scales and biases bf16 bit patterns uint16 [rows][K/64].
  * Packed layout: the NVFP4 block (4608 B per 64 rows x 128 K) with the same
- * 4096 B of codes, then for row n of the tile the 32 bytes at 4096 + 32n:
+ * 4096 B of code dwords, each holding its 8 codes (k0..k7) as k0 k2 k4 k6 in
+ * bits 0-15 and k1 k3 k5 k7 in bits 16-31 (4 bits each, ascending), then for
+ * row n of the tile the 32 bytes at 4096 + 32n:
  * for sub-tile t = 0..3 and group h = 0, 1 of the iteration one dword
  * holding scale (low half) and bias (high half). gate_up = 1 pairs gate and
  * up rows exactly as vq_pack_nvfp4 does. */

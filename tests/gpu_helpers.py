@@ -127,14 +127,22 @@ def pack_fp8_np(w):
 
 def pack_affine_np(codes, scales_bits, biases_bits, gate_up=False):
     """Affine 4-bit packed layout from include/libverify.h: the NVFP4 code
-    layout, then per tile row n 32 bytes of (scale, bias) dwords for sub-tiles
-    t = 0..3 and groups h = 0, 1."""
+    layout with every code dword in the affine nibble order, then per tile
+    row n 32 bytes of (scale, bias) dwords for sub-tiles t = 0..3 and groups
+    h = 0, 1."""
     rows, kh = codes.shape
     I = 2 * kh // 128
     rmap = _row_map(rows, gate_up)
     T = rmap.shape[0]
     c = _gather(codes, rmap).reshape(T, 4, 16, I, 4, 4, 4)       # T t n I j g b
-    c = c.transpose(0, 3, 1, 5, 2, 4, 6).reshape(T, I, 4096)
+    c = c.transpose(0, 3, 1, 5, 2, 4, 6).reshape(T, I, 1024, 4)
+    # each code dword in the affine nibble order: even-k nibbles then odd-k
+    lo, hi = c & 0x0F, c >> 4
+    word = np.zeros(c.shape[:-1], dtype=np.uint32)
+    for b in range(4):
+        word |= lo[..., b].astype(np.uint32) << (4 * b)
+        word |= hi[..., b].astype(np.uint32) << (16 + 4 * b)
+    c = word.astype("<u4").view(np.uint8).reshape(T, I, 4096)
     pair = (scales_bits.astype(np.uint32) | (biases_bits.astype(np.uint32) << 16))  # [rows][K/64]
     pw = _gather(pair, rmap).reshape(T, 4, 16, I, 2)                 # T t n I h
     pw = pw.transpose(0, 3, 2, 1, 4).reshape(T, I, 16 * 8)           # T I n t h (dwords)
