@@ -281,6 +281,77 @@ def affine_q4(torch, ops, inputs_mod, dev, layers=4, rows=(8, 32), reps=3):
     return out
 
 
+# The draft side of a step: the 5-layer draft (hidden 5,120; per layer a
+# 6,144-row qkv projection, two 1,280-row dynamic projections, a 5,120 x 4,096
+# attention output projection and a SwiGLU MLP of 17,408) after the context
+# projection that reads five target layers at once (5,120 x 25,600), then the
+# target's vocabulary head, which the draft shares. NVFP4 weights, 8 query rows.
+DRAFT_LAYERS = 5
+DRAFT_SHAPES = [("draft_qkv", "nvfp4", 6144, HIDDEN), ("draft_dyn_a", "nvfp4", 1280, HIDDEN),
+                ("draft_dyn_b", "nvfp4", 1280, HIDDEN), ("draft_attn_o", "nvfp4", HIDDEN, 4096),
+                ("draft_gate_up", "nvfp4_silu", INTER, HIDDEN), ("draft_down", "nvfp4", HIDDEN, INTER)]
+DRAFT_CTX = ("draft_context", "nvfp4", HIDDEN, 5 * HIDDEN)
+
+
+def draft_stream(torch, ops, inputs_mod, p, steps=10):
+    """One draft block's weight stream, captured in a graph and replayed: the
+    context projection, the 5 draft layers and the shared vocabulary head
+    (with argmax: the draft's proposals), at M = 8."""
+    dev = p.dev
+    items = [DRAFT_CTX] + [s for _ in range(DRAFT_LAYERS) for s in DRAFT_SHAPES]
+    w = []
+    for i, (kind, fmt, n, k) in enumerate(items):
+        key = (5, 6000, i)
+        if fmt == "nvfp4_silu":
+            c, sc = inputs_mod.device_nvfp4_weights(key, 2 * n, k, dev)
+            w.append(ops.pack_nvfp4(c, sc, gate_up=True))
+        else:
+            c, sc = inputs_mod.device_nvfp4_weights(key, n, k, dev)
+            w.append(ops.pack_nvfp4(c, sc))
+        del c, sc
+    m = M_ROWS
+    bf = torch.bfloat16
+    xs = {k: inputs_mod.device_x_bf16((5, 6100, k), m, k, dev) for k in (HIDDEN, 4096, INTER, 5 * HIDDEN)}
+    ys = {n: torch.empty((m, n), dtype=bf, device=dev) for n in (6144, 1280, HIDDEN, INTER)}
+    ws = {}
+    for kind, fmt, n, k in items:
+        op = ops.VQ_OP_NVFP4_SILU_MUL if fmt == "nvfp4_silu" else ops.VQ_OP_NVFP4
+        if (op, n, k) not in ws:
+            ws[(op, n, k)] = ops.workspace(op, m, n, k, dev)
+    head = len(p.items) - 1
+
+    def run():
+        for (kind, fmt, n, k), wi in zip(items, w):
+            if fmt == "nvfp4_silu":
+                ops.vq_gemm_nvfp4(xs[k], wi, 1.0, ys[n], epilogue=ops.VQ_EPI_SILU_MUL,
+                                  workspace=ws[(ops.VQ_OP_NVFP4_SILU_MUL, n, k)])
+            else:
+                ops.vq_gemm_nvfp4(xs[k], wi, 1.0, ys[n], workspace=ws[(ops.VQ_OP_NVFP4, n, k)])
+        p.launch(head)
+
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        run()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            run()
+    torch.cuda.current_stream().wait_stream(st)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    nbytes = sum(weight_bytes(f, n, k) for _, f, n, k in items) + weight_bytes("nvfp4", VOCAB, HIDDEN)
+    del w
+    torch.cuda.empty_cache()
+    return {"rows": m, "launches": len(items) + 1, "weight_bytes": nbytes, "ms_per_block": round(dt * 1e3, 4),
+            "gbps": round(nbytes / dt / 1e9, 1)}
+
+
 def sampled_verify(torch, ops, inputs_mod, p, g_steps=10, reps=20):
     """The end of the pass at nonzero temperature (temperature 1, top_k 32,
     top_p 0.95): the head also writes fp32 logits and vq_sample_accept reads
@@ -545,6 +616,8 @@ def main():
     sweep = m_sweep(torch, ops, inputs, p)
     sampled = sampled_verify(torch, ops, inputs, p)
     affine = affine_q4(torch, ops, inputs, dev)
+    draft = draft_stream(torch, ops, inputs, p)
+    log(f"draft block: {draft['ms_per_block']:.3f} ms, {draft['gbps']:.0f} GB/s")
     log(f"affine 4-bit MLP at M=8: {affine['8']}")
     log(f"sampled verify: pass {sampled['ms_per_pass_sampled']:.3f} ms, sampler {sampled['sampler_us']:.1f} us")
     gu_w = weight_bytes("nvfp4_silu", INTER, HIDDEN)
@@ -588,6 +661,7 @@ def main():
         "m_sweep_weight_gbps": sweep,
         "sampled_verify": sampled,
         "affine_q4_mlp": affine,
+        "draft_block": draft,
         "roofline": {
             "kernel": "vq_gemm_kernel<NVFP4, SILU_MUL, M<=8> ([gate;up] 34816x5120 + SiLU*up)",
             "bound": "hbm",

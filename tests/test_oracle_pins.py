@@ -347,6 +347,17 @@ def test_nine_bytes_per_sixteen_and_splash_geometry():
     assert sum(s["attn_in_widths"]) == O.ATTN_QG + 2 * O.ATTN_KV
 
 
+def test_draft_geometry_bytes():
+    # the draft's layer bytes from its printed widths: qkv, two dynamic
+    # projections, the attention output projection and a SwiGLU MLP
+    d = _gold("pages_numbers.json")["splash_draft_geometry"]
+    h = d["hidden"]
+    layer = (O.bytes_nvfp4(d["qkv"], h) + 2 * O.bytes_nvfp4(d["dynamic"], h) + O.bytes_nvfp4(h, d["attn"])
+             + 2 * O.bytes_nvfp4(d["swiglu"], h) + O.bytes_nvfp4(h, d["swiglu"]))
+    assert round(layer / 1e6, 1) == d["layer_mb"]
+    assert round(O.bytes_nvfp4(*d["context_proj_shape"]) / 1e6, 2) == d["context_proj_mb"]
+
+
 def test_schedule_shape():
     sch = O.pass_schedule()
     assert len(sch) == 257
