@@ -282,13 +282,13 @@ def affine_q4(torch, ops, inputs_mod, dev, layers=4, rows=(8, 32), reps=3):
 
 
 # The draft side of a step: the 5-layer draft (hidden 5,120; per layer a
-# 6,144-row qkv projection, two 1,280-row dynamic projections, a 5,120 x 4,096
-# attention output projection and a SwiGLU MLP of 17,408) after the context
-# projection that reads five target layers at once (5,120 x 25,600), then the
-# target's vocabulary head, which the draft shares. NVFP4 weights, 8 query rows.
+# 6,144-row qkv projection and two 1,280-row dynamic projections, which read
+# the same input and run as one 8,704-row matrix, a 5,120 x 4,096 attention
+# output projection and a SwiGLU MLP of 17,408) after the context projection
+# that reads five target layers at once (5,120 x 25,600), then the target's
+# vocabulary head, which the draft shares. NVFP4 weights, 8 query rows.
 DRAFT_LAYERS = 5
-DRAFT_SHAPES = [("draft_qkv", "nvfp4", 6144, HIDDEN), ("draft_dyn_a", "nvfp4", 1280, HIDDEN),
-                ("draft_dyn_b", "nvfp4", 1280, HIDDEN), ("draft_attn_o", "nvfp4", HIDDEN, 4096),
+DRAFT_SHAPES = [("draft_qkv_dyn", "nvfp4", 6144 + 2 * 1280, HIDDEN), ("draft_attn_o", "nvfp4", HIDDEN, 4096),
                 ("draft_gate_up", "nvfp4_silu", INTER, HIDDEN), ("draft_down", "nvfp4", HIDDEN, INTER)]
 DRAFT_CTX = ("draft_context", "nvfp4", HIDDEN, 5 * HIDDEN)
 
@@ -312,7 +312,7 @@ def draft_stream(torch, ops, inputs_mod, p, steps=10):
     m = M_ROWS
     bf = torch.bfloat16
     xs = {k: inputs_mod.device_x_bf16((5, 6100, k), m, k, dev) for k in (HIDDEN, 4096, INTER, 5 * HIDDEN)}
-    ys = {n: torch.empty((m, n), dtype=bf, device=dev) for n in (6144, 1280, HIDDEN, INTER)}
+    ys = {n: torch.empty((m, n), dtype=bf, device=dev) for n in (6144 + 2 * 1280, HIDDEN, INTER)}
     ws = {}
     for kind, fmt, n, k in items:
         op = ops.VQ_OP_NVFP4_SILU_MUL if fmt == "nvfp4_silu" else ops.VQ_OP_NVFP4

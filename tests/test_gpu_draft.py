@@ -13,7 +13,7 @@ from tests.gpu_helpers import check_f32, say, to_dev_bf16, to_dev_u8, torch_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("m,n,k", [(8, 1280, 5120), (8, 6144, 5120), (8, 5120, 4096), (16, 1280, 5120),
+@pytest.mark.parametrize("m,n,k", [(8, 1280, 5120), (8, 8704, 5120), (8, 5120, 4096), (16, 1280, 5120),
                                    (8, 5120, 25600), (32, 5120, 25600)])
 def test_draft_shapes_nvfp4(m, n, k):
     from bit_block_scaled_vq_amd import ops
