@@ -1,7 +1,8 @@
 // HIP kernels (gfx950 / CDNA4) for the weight stream of the speculative-decoding
-// verify pass: a one-time weight pack, NVFP4 and FP8 E4M3 skinny GEMMs
-// (M <= 32 rows) with a stream-K schedule and a fixed-order split-K reduction,
-// the vocabulary-head argmax + greedy-accept epilogue, and two HBM probes.
+// verify pass: a one-time weight pack, NVFP4, FP8 E4M3 and affine 4-bit
+// skinny GEMMs (M <= 32 rows) with a stream-K schedule and a fixed-order
+// split-K reduction, the vocabulary-head argmax + greedy-accept epilogue, and
+// two HBM probes.
 //
 // Method: "lithos-metal: per-layer megakernels for Qwen3.8-27B on an M5 Max ..."
 // (sections "What one token costs the bus", "How DSpark is wired in",
@@ -30,8 +31,17 @@
 //    scale (one fp32 FMA) and lanes l, l+32 are added once per tile piece.
 //    gfx950's packed fp4 -> bf16 convert applies only the exponent of its
 //    scale operand, so a non-power-of-two E4M3 scale cannot be folded into it.
+//  * NVFP4 with more than 8 rows: the same weights scaled in registers (exact
+//    in bf16), 16 activation rows per MFMA.
 //  * FP8: the MFMA accumulates directly; the per-tensor scale is applied in
 //    the epilogue.
+//  * Affine 4-bit (scale * q + bias per 64 K, "144 tok/s needs 502 GB/s ...",
+//    section "The engine hard-codes the model"): nibbles decode to bf16
+//    128 + q with one mask-and-or per two weights; the group sums of X come
+//    from MFMAs against ones, and s * (x . (128+q)) + (b - 128 s) * sum(x) is
+//    accumulated in fp32.
+//  * Weights stream with non-temporal 16-byte loads, 3 iterations in flight
+//    per wave.
 //  * Stream-K over 4-wave workgroups: workgroup g owns iterations
 //    [g*W/G, (g+1)*W/G) of the (tile, iteration) space and each wave a
 //    contiguous quarter of that. Tiles shared by waves of one workgroup are
