@@ -135,3 +135,33 @@ def test_affine_full_size_down_projection_sampled_columns():
         res = run_affine(x, None, None, None, n, out="f32", w=w)
         ref = O.gemm_affine_q4(x, codes, sb, bb, rows=cols)
         check_f32(res["f32"][:, cols], ref, what=f"affine down M={m}")
+
+
+def test_affine_graph_replay_matches_eager():
+    torch, dev = torch_dev()
+    ops = _ops()
+    m, inter, k = 8, 1024, 2048
+    x = inputs.x_bf16((460,), m, k)
+    codes, sb, bb = inputs.affine_weights((460,), 2 * inter, k)
+    w = pack(codes, sb, bb, gate_up=True)
+    xd = to_dev_bf16(x)
+    ws = ops.workspace(ops.VQ_OP_AFFINE_Q4_SILU_MUL, m, inter, k, dev)
+    ye = torch.empty((m, inter), dtype=torch.float32, device=dev)
+    ops.vq_gemm_affine_q4(xd, w, ye, epilogue=ops.VQ_EPI_SILU_MUL, workspace=ws)
+    eager = ye.cpu().numpy()
+    y = torch.zeros_like(ye)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            ops.vq_gemm_affine_q4(xd, w, y, epilogue=ops.VQ_EPI_SILU_MUL, workspace=ws)
+    torch.cuda.current_stream().wait_stream(st)
+    for i in range(4):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), eager), i
+        ops.vq_gemm_affine_q4(xd, w, ye, epilogue=ops.VQ_EPI_SILU_MUL, workspace=ws)
+        torch.cuda.synchronize()

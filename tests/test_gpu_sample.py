@@ -445,3 +445,43 @@ def test_binding_rejections():
                              workspace=ops.workspace(ops.VQ_OP_SAMPLE, 8, 100, 0, dev))
     with pytest.raises(ops.VerifyError):  # no workspace
         ops.vq_sample_accept(lg, 1, 8, 1.0, 32, 1.0, u, acc, draft=torch.zeros(7, dtype=torch.int32, device=dev))
+
+
+def test_graph_replay_matches_eager():
+    # the sampler inside a captured graph, replayed with eager calls on the
+    # same workspace in between: every replay equals the eager result (the
+    # per-lane counters are reset by the lane's last row each time)
+    torch, dev = _dev()
+    lanes, R, V = 4, 8, 40000
+    M = lanes * R
+    z = inputs.logits_f32((83,), M, V)
+    u = inputs.uniforms((83,), M)
+    ua = inputs.uniforms((83, 1), M)
+    q, d = _spec_inputs((83,), z, lanes, R, 0.8, 32, 0.9)
+    ws = ops.workspace(ops.VQ_OP_SAMPLE, M, V, 0, dev)
+    say("case graph replay")
+    eager = run_gpu(z, lanes, R, 0.8, 32, 0.9, u, draft=d, q=q, u_accept=ua, ws=ws)
+    lg, uu, uaa = _f32(z), _f32(u), _f32(ua)
+    dd, qi, qp = _i32(d), _i32(q[0]), _f32(q[1])
+    tok = torch.full((M,), -7, dtype=torch.int32, device=dev)
+    acc = torch.full((lanes,), -7, dtype=torch.int32, device=dev)
+    commit = torch.full((lanes, R), -7, dtype=torch.int32, device=dev)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            ops.vq_sample_accept(lg, lanes, R, 0.8, 32, 0.9, uu, acc, draft=dd, draft_ids=qi, draft_probs=qp,
+                                 u_accept=uaa, token_out=tok, commit_out=commit, workspace=ws)
+    torch.cuda.current_stream().wait_stream(st)
+    for i in range(4):
+        tok.fill_(-7)
+        acc.fill_(-7)
+        commit.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(tok.cpu().numpy(), eager["tok"]), i
+        assert np.array_equal(acc.cpu().numpy(), eager["acc"]), i
+        assert np.array_equal(commit.cpu().numpy(), eager["commit"]), i
+        run_gpu(z, lanes, R, 0.8, 32, 0.9, u, draft=d, ws=ws)  # eager work between replays
