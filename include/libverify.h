@@ -62,7 +62,8 @@
  *     returns VQ_ERR_WORKSPACE; the schedule never changes silently.
  *   - Results are deterministic: the K partition and the order of the fixed
  *     split-K reduction depend only on (N, K) and the epilogue, never on M.
- *     FP8: row r of an M-row call equals row r of any other M bit for bit.
+ *     FP8 and affine 4-bit: row r of an M-row call equals row r of any other
+ *     M bit for bit.
  *     NVFP4 has two compute families with different rounding (M <= 8: the
  *     block scale multiplies each block's fp32 partial sum; M > 8: the weights
  *     are scaled before the MFMA, exactly, and summed in fp32), and rows agree
@@ -91,7 +92,8 @@ typedef enum {
   VQ_ERR_WORKSPACE = 4, /* workspace NULL or smaller than vq_workspace_bytes() */
   VQ_ERR_DEVICE = 5,    /* no HIP device, or the current device is not gfx950 */
   VQ_ERR_LAUNCH = 6,    /* the kernel launch failed */
-  VQ_ERR_VALUE = 7      /* an enum argument has an unknown value */
+  VQ_ERR_VALUE = 7      /* an enum argument is unknown, or a sampling parameter
+                           (temperature, top_k, top_p) is out of range */
 } vq_status;
 
 typedef enum { VQ_OUT_BF16 = 0, VQ_OUT_F32 = 1 } vq_out_dtype;
