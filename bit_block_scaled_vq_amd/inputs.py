@@ -14,6 +14,10 @@ Distributions (the synthetic stand-in for the 27B checkpoint the pages read):
   * FP8 projection weights: N(0, 0.02) rounded to E4M3FN;
   * drafts: draft j equals the target argmax of row j with probability 0.7,
     otherwise a uniform token id in [0, V).
+  * Gated DeltaNet state stream (fp32): state N(0, 0.05); queries and keys
+    unit vectors (normalised Gaussians, as after the Q/K norm); values
+    N(0, 1); decays exp(-|N(0, 0.1)|) in (0, 1]; write strengths
+    sigmoid(N(0, 1)) in (0, 1).
 
 Host generation uses numpy PCG64 with one SeedSequence per (key..., chunk)
 so any chunk of any tensor can be regenerated on its own. Device generation
@@ -42,6 +46,7 @@ T_LOGITS = 5
 T_UNIFORM = 6
 T_DRAFT_Q = 7
 T_AFFINE = 8
+T_GDN = 9
 
 LOGIT_STD = 2.5
 
@@ -189,6 +194,21 @@ def draft_distributions(key, preferred, vocab: int, n: int = 16):
     return ids, probs, toks
 
 
+def gdn_inputs(key, B: int, T: int, H: int, Hk: int, dk: int = 128, dv: int = 128):
+    """(state, q, k, v, a, b) as fp32 arrays: state [B][H][dk][dv],
+    q, k [B][T][Hk][dk], v [B][T][H][dv], a, b [B][T][H]."""
+    g = rng(*key, T_GDN)
+    state = (g.standard_normal((B, H, dk, dv)) * 0.05).astype(np.float32)
+    q = g.standard_normal((B, T, Hk, dk))
+    k = g.standard_normal((B, T, Hk, dk))
+    q = (q / np.linalg.norm(q, axis=-1, keepdims=True)).astype(np.float32)
+    k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+    v = g.standard_normal((B, T, H, dv)).astype(np.float32)
+    a = np.exp(-np.abs(g.standard_normal((B, T, H)) * 0.1)).astype(np.float32)
+    b = (1.0 / (1.0 + np.exp(-g.standard_normal((B, T, H))))).astype(np.float32)
+    return state, q, k, v, a, b
+
+
 # -------------------------------------------------------------- device side
 
 def _torch_gen(device, *key):
@@ -247,3 +267,19 @@ def device_drafts(key, argmax_rows, vocab: int, p: float = DRAFT_P):
     u = torch.rand((lanes, r - 1), generator=g, device=a.device)
     ids = torch.randint(0, vocab, (lanes, r - 1), generator=g, device=a.device)
     return torch.where(u < p, a[:, : r - 1], ids).to(torch.int32).contiguous()
+
+
+def device_gdn_inputs(key, B: int, T: int, H: int, Hk: int, device, dk: int = 128, dv: int = 128):
+    """Same distributions as gdn_inputs, drawn on the device (fp32 tensors)."""
+    torch = _torch()
+    g = _torch_gen(device, *key, T_GDN)
+    f = dict(generator=g, device=device, dtype=torch.float32)
+    state = torch.randn((B, H, dk, dv), **f).mul_(0.05)
+    q = torch.randn((B, T, Hk, dk), **f)
+    k = torch.randn((B, T, Hk, dk), **f)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = torch.randn((B, T, H, dv), **f)
+    a = torch.exp(-torch.randn((B, T, H), **f).mul_(0.1).abs_())
+    b = torch.sigmoid(torch.randn((B, T, H), **f))
+    return state, q.contiguous(), k.contiguous(), v, a, b

@@ -6,3 +6,4 @@ its Python binding) never imports, links or calls anything under ``oracle/``.
 """
 from .verify_oracle import *  # noqa: F401,F403
 from .sampling_oracle import *  # noqa: F401,F403
+from .gdn_oracle import *  # noqa: F401,F403
