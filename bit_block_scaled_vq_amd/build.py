@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libverify.so")
 SOURCES = [os.path.join(CSRC, "libverify.cpp"), os.path.join(CSRC, "vq_kernels.hip"),
-           os.path.join(CSRC, "vq_sample.hip")]
+           os.path.join(CSRC, "vq_sample.hip"), os.path.join(CSRC, "vq_gdn.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -512,6 +512,68 @@ int32_t vq_sample_accept(const float* logits, int32_t lanes, int32_t R, int32_t 
   return VQ_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+int32_t gdn_call(const char* fn, const float* state_in, float* state_out, const float* q, const float* k,
+                 const float* v, const float* a, const float* b, float* o, const int32_t* count, int32_t lanes,
+                 int32_t B, int32_t T, int32_t H, int32_t Hk, void* stream) {
+  if (!state_in || !state_out || !q || !k || !v || !a || !b)
+    return fail(VQ_ERR_NULL, "%s: state_in, state_out, q, k, v, a and b are required", fn);
+  if (B < 1 || T < 1 || T > vq::kGdnMaxT || H < 1 || Hk < 1 || Hk > H || H % Hk != 0 ||
+      (int64_t)B * H > (1 << 24))
+    return fail(VQ_ERR_SHAPE, "%s: B = %d, T = %d, H = %d, Hk = %d out of range (1 <= T <= %d, Hk divides H)", fn,
+                B, T, H, Hk, vq::kGdnMaxT);
+  if (lanes < 1 || lanes > 4 || B % lanes != 0)
+    return fail(VQ_ERR_SHAPE, "%s: lanes = %d must lie in [1, 4] and divide B = %d", fn, lanes, B);
+  if (!aligned(q, 16) || !aligned(k, 16)) return fail(VQ_ERR_ALIGN, "%s: q and k must be 16-byte aligned", fn);
+  const void* arrays[] = {state_in, state_out, v, a, b, o, count};
+  for (const void* x : arrays)
+    if (x && !aligned(x, 4)) return fail(VQ_ERR_ALIGN, "%s: fp32/int32 arrays must be 4-byte aligned", fn);
+  const size_t sbytes = (size_t)B * H * vq::kGdnDk * vq::kGdnDv * sizeof(float);
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(state_in), o0 = reinterpret_cast<uintptr_t>(state_out);
+  if (i0 < o0 + sbytes && o0 < i0 + sbytes) return fail(VQ_ERR_VALUE, "%s: state_in and state_out overlap", fn);
+  int32_t st = check_device();
+  if (st) return st;
+  vq::GdnParams p{};
+  p.state_in = state_in;
+  p.state_out = state_out;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.a = a;
+  p.b = b;
+  p.o = o;
+  p.count = count;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.Hk = Hk;
+  p.lanes = lanes;
+  const int err = vq::launch_gdn(p, stream);
+  if (err) return fail(VQ_ERR_LAUNCH, "%s: kernel launch failed: %s", fn, hipGetErrorString((hipError_t)err));
+  return VQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t vq_gdn_verify(const float* state_in, float* state_out, const float* q, const float* k, const float* v,
+                      const float* a, const float* b, float* o, int32_t B, int32_t T, int32_t H, int32_t Hk,
+                      void* stream) {
+  return gdn_call("vq_gdn_verify", state_in, state_out, q, k, v, a, b, o, nullptr, 1, B, T, H, Hk, stream);
+}
+
+int32_t vq_gdn_commit(const float* state_in, float* state_out, const float* q, const float* k, const float* v,
+                      const float* a, const float* b, const int32_t* accept_len, int32_t lanes, int32_t B,
+                      int32_t T, int32_t H, int32_t Hk, void* stream) {
+  if (!accept_len) return fail(VQ_ERR_NULL, "vq_gdn_commit: accept_len is required");
+  return gdn_call("vq_gdn_commit", state_in, state_out, q, k, v, a, b, nullptr, accept_len, lanes, B, T, H, Hk,
+                  stream);
+}
+
 int32_t vq_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (!src || !dst) return fail(VQ_ERR_NULL, "vq_probe_copy: src and dst are required");
   if (bytes == 0 || bytes % 16) return fail(VQ_ERR_SHAPE, "bytes must be a positive multiple of 16");

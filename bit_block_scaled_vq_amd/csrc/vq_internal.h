@@ -123,10 +123,29 @@ struct SampleParams {
   uint32_t* lane_count;              // workspace: [4] rows finished per lane
 };
 
+// Gated DeltaNet state stream: fp32 state per value head, dk x dv.
+constexpr int kGdnDk = 128;
+constexpr int kGdnDv = 128;
+constexpr int kGdnMaxT = 16;         // rows per entry and call
+
+struct GdnParams {
+  const float* state_in;             // [B][H][dk][dv]
+  float* state_out;                  // [B][H][dk][dv], disjoint from state_in
+  const float* q;                    // [B][T][Hk][dk]
+  const float* k;                    // [B][T][Hk][dk]
+  const float* v;                    // [B][T][H][dv]
+  const float* a;                    // [B][T][H] decays
+  const float* b;                    // [B][T][H] write strengths
+  float* o;                          // [B][T][H][dv] or null
+  const int32_t* count;              // [lanes] rows to re-scan (commit) or null (verify)
+  int32_t B, T, H, Hk, lanes;
+};
+
 // Launchers: return 0 on success, else the hipError_t of the launch.
 int launch_gemm(int fmt, int epi, const GemmParams& p, void* stream);
 int launch_pack(int fmt, const PackParams& p, void* stream);
 int launch_sample(const SampleParams& p, void* stream);
+int launch_gdn(const GdnParams& p, void* stream);
 int launch_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 int launch_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 

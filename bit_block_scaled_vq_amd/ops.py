@@ -42,7 +42,8 @@ VQ_PACK_AFFINE_Q4_GATE_UP = 4
 
 EXPORTS = [
     "vq_packed_bytes", "vq_pack_nvfp4", "vq_pack_fp8", "vq_pack_affine_q4", "vq_gemm_affine_q4",
-    "vq_gemm_nvfp4", "vq_gemm_fp8", "vq_lmhead_argmax_accept", "vq_sample_accept", "vq_workspace_bytes",
+    "vq_gemm_nvfp4", "vq_gemm_fp8", "vq_lmhead_argmax_accept", "vq_sample_accept", "vq_gdn_verify",
+    "vq_gdn_commit", "vq_workspace_bytes",
     "vq_status_str", "vq_last_error", "vq_abi_version", "vq_probe_copy", "vq_probe_read",
 ]
 
@@ -84,6 +85,10 @@ def lib() -> ctypes.CDLL:
     L.vq_lmhead_argmax_accept.restype = i32
     L.vq_sample_accept.argtypes = [vp, i32, i32, i32, f32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.vq_sample_accept.restype = i32
+    L.vq_gdn_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+    L.vq_gdn_verify.restype = i32
+    L.vq_gdn_commit.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    L.vq_gdn_commit.restype = i32
     L.vq_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.vq_workspace_bytes.restype = sz
     L.vq_status_str.argtypes = [i32]
@@ -341,6 +346,54 @@ def vq_sample_accept(logits, lanes: int, R: int, temperature: float, top_k: int,
         _ptr(logits), lanes, R, V, float(temperature), int(top_k), float(top_p), _ptr(draft), _ptr(draft_ids),
         _ptr(draft_probs), _ptr(u_accept), _ptr(u_draw), _ptr(token_out), _ptr(accept_len_out),
         _ptr(commit_out), _ptr(cand_out), _ptr(prob_out), ws_ptr, ws_n, _stream(stream)))
+
+
+def _gdn_args(state_in, state_out, q, k, v, a, b, o=None):
+    torch = _torch()
+    f32 = (torch.float32,)
+    _need(state_in, "state_in", f32, 4)
+    _need(state_out, "state_out", f32, 4)
+    B, H, dk, dv = state_in.shape
+    if state_out.shape != state_in.shape or (dk, dv) != (128, 128):
+        raise ValueError("states must be [B][H][128][128] fp32 and of the same shape")
+    _need(q, "q", f32, 4)
+    _need(k, "k", f32, 4)
+    T, Hk = q.shape[1], q.shape[2]
+    if q.shape != (B, T, Hk, 128) or k.shape != q.shape:
+        raise ValueError("q and k must be [B][T][Hk][128]")
+    _need(v, "v", f32, 4)
+    if v.shape != (B, T, H, 128):
+        raise ValueError("v must be [B][T][H][128]")
+    for name, t in (("a", a), ("b", b)):
+        _need(t, name, f32, 3)
+        if t.shape != (B, T, H):
+            raise ValueError(f"{name} must be [B][T][H]")
+    if o is not None:
+        _need(o, "o", f32, 4)
+        if o.shape != v.shape:
+            raise ValueError("o must be [B][T][H][128]")
+    return B, T, H, Hk
+
+
+def vq_gdn_verify(state_in, state_out, q, k, v, a, b, o=None, stream=None):
+    """Gated DeltaNet state stream of the verify pass: every entry scans its T
+    rows from state_in and writes the final state to state_out (the other
+    parity slot) and, if given, the row outputs to o."""
+    B, T, H, Hk = _gdn_args(state_in, state_out, q, k, v, a, b, o)
+    _check(lib().vq_gdn_verify(_ptr(state_in), _ptr(state_out), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                               _ptr(o), B, T, H, Hk, _stream(stream)))
+
+
+def vq_gdn_commit(state_in, state_out, q, k, v, a, b, accept_len, lanes: int, stream=None):
+    """Commit pass: entries whose lane accepted fewer than T rows get the
+    re-scan of their accepted rows from state_in; the others keep state_out."""
+    torch = _torch()
+    B, T, H, Hk = _gdn_args(state_in, state_out, q, k, v, a, b)
+    _need(accept_len, "accept_len", (torch.int32,))
+    if accept_len.numel() != lanes:
+        raise ValueError("accept_len must hold one count per lane")
+    _check(lib().vq_gdn_commit(_ptr(state_in), _ptr(state_out), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                               _ptr(accept_len), lanes, B, T, H, Hk, _stream(stream)))
 
 
 def vq_probe_copy(src, dst, stream=None):

@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define VQ_ABI_VERSION 4
+#define VQ_ABI_VERSION 5
 
 typedef enum {
   VQ_OK = 0,
@@ -265,6 +265,59 @@ int32_t vq_sample_accept(const float* logits, int32_t lanes, int32_t R, int32_t 
                          int32_t* token_out, int32_t* accept_len_out, int32_t* commit_out,
                          int32_t* cand_out, float* prob_out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gated DeltaNet state stream of the verify pass, out of place between two
+ * parity slots of the fp32 recurrent state ("Beating Splash on an M5 Max
+ * ...", section "What actually moved the needle": the fused GDN step writes
+ * from parity buffer A to B, a fully accepted round flips the parity, a
+ * partly rejected one re-scans only the committed rows from the intact
+ * previous parity; "lithos-metal ...", section "What one token costs the
+ * bus": the state is fp32 (v_heads, dk, dv) = (48, 128, 128) per GDN layer,
+ * read and written once per pass; section "How DSpark is wired in": the
+ * commit pass recomputes the recurrence from the slot the verify read over
+ * the committed tokens, whose count the accept scan wrote). The pages print
+ * no recurrence; it is the gated delta rule of Yang, Kautz and Hatamizadeh,
+ * "Gated Delta Networks: Improving Mamba2 with Delta Rule" (ICLR 2025), per
+ * value head in the (dk, dv) layout:
+ *     S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,  o_t = S_t^T q_t
+ * Queries, keys and values arrive already convolved and normalised, and the
+ * decays a_t and write strengths b_t already computed: the 4-tap
+ * convolution, the Q/K norm and the gate formulas are not part of this call.
+ *
+ * B entries (e.g. layers x lanes, entry-major with entry e = layer * lanes +
+ * lane) of T rows each; dk = dv = 128; H value heads share Hk key heads
+ * (Hk divides H; value head h reads key head h / (H / Hk)).
+ *   state_in   fp32 [B][H][128][128]: the slot read (never written)
+ *   state_out  fp32 [B][H][128][128]: the slot written; must not overlap
+ *              state_in
+ *   q, k       fp32 [B][T][Hk][128], 16-byte aligned
+ *   v          fp32 [B][T][H][128]
+ *   a, b       fp32 [B][T][H]: decay and write strength of each row and head
+ *   o          fp32 [B][T][H][128] or NULL: the output of every row
+ * Shapes: 1 <= B, 1 <= T <= 16, 1 <= Hk <= H, H % Hk == 0, B * H <= 2^24.
+ * All arrays 4-byte aligned (q, k 16-byte). One launch on `stream`, no
+ * workspace; fp32 arithmetic with every sum in a fixed order, and the row
+ * partition does not depend on B, so an entry's result is bitwise the same
+ * whatever B is.
+ *
+ * vq_gdn_verify: every entry scans all T rows from state_in, writes the
+ * final state to state_out and, when o is given, the T outputs. */
+int32_t vq_gdn_verify(const float* state_in, float* state_out, const float* q, const float* k,
+                      const float* v, const float* a, const float* b, float* o,
+                      int32_t B, int32_t T, int32_t H, int32_t Hk, void* stream);
+
+/* vq_gdn_commit: the commit pass after the accept scan. Entry e belongs to
+ * lane e % lanes and c = accept_len[lane] (device int32 [lanes], as written
+ * by vq_lmhead_argmax_accept or vq_sample_accept), clamped to [0, T]. An
+ * entry with c = T is left alone (state_out already holds what
+ * vq_gdn_verify wrote); any other entry gets the scan of its first c rows
+ * from state_in (c = 0 copies it). The inputs are the same arrays the verify
+ * call read. For each entry the result is bitwise what vq_gdn_verify over
+ * those c rows writes (the rollback identity). 1 <= lanes <= 4, B % lanes
+ * == 0; other shapes as above. */
+int32_t vq_gdn_commit(const float* state_in, float* state_out, const float* q, const float* k,
+                      const float* v, const float* a, const float* b, const int32_t* accept_len,
+                      int32_t lanes, int32_t B, int32_t T, int32_t H, int32_t Hk, void* stream);
 
 /* Workspace bytes needed by `op` at this shape (for VQ_OP_NVFP4_SILU_MUL, N is
  * the output width, i.e. half the weight rows; for VQ_OP_LMHEAD, N = V and

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = ops.lib()
-    assert L.vq_abi_version() == 4
+    assert L.vq_abi_version() == 5
     assert ops.status_str(ops.VQ_OK) == "VQ_OK"
     assert ops.status_str(ops.VQ_ERR_WORKSPACE) == "VQ_ERR_WORKSPACE"
     assert ops.status_str(99) == "VQ_ERR_UNKNOWN"
@@ -216,12 +216,52 @@ def _gpu_visible():
         return False
 
 
+S0 = 1 << 32           # fake state slots, far enough apart not to overlap
+S1 = S0 + (1 << 31)
+
+
+def _gdn(si=S0, so=S1, q=A, k=A, v=A, a=A, b=A, o=A, B=2, T=8, H=48, Hk=16):
+    return ops.lib().vq_gdn_verify(si, so, q, k, v, a, b, o, B, T, H, Hk, None)
+
+
+def _commit(acc=A, lanes=2, B=4, T=8, H=48, Hk=16, si=S0, so=S1):
+    return ops.lib().vq_gdn_commit(si, so, A, A, A, A, A, acc, lanes, B, T, H, Hk, None)
+
+
+def test_gdn_validation():
+    assert _gdn(si=None) == ops.VQ_ERR_NULL
+    assert _gdn(k=None) == ops.VQ_ERR_NULL
+    assert _gdn(b=None) == ops.VQ_ERR_NULL
+    assert _gdn(B=0) == ops.VQ_ERR_SHAPE
+    assert _gdn(T=0) == ops.VQ_ERR_SHAPE
+    assert _gdn(T=17) == ops.VQ_ERR_SHAPE
+    assert _gdn(Hk=0) == ops.VQ_ERR_SHAPE
+    assert _gdn(H=48, Hk=96) == ops.VQ_ERR_SHAPE
+    assert _gdn(H=48, Hk=5) == ops.VQ_ERR_SHAPE
+    assert _gdn(q=A + 4) == ops.VQ_ERR_ALIGN
+    assert _gdn(k=A + 8) == ops.VQ_ERR_ALIGN
+    assert _gdn(v=A + 2) == ops.VQ_ERR_ALIGN
+    assert _gdn(o=A + 1) == ops.VQ_ERR_ALIGN
+    # the two slots must not overlap: 2 entries x 48 heads x 64 KiB = 6 MiB
+    assert _gdn(so=S0 + (6 << 20) - 4) == ops.VQ_ERR_VALUE
+    assert _gdn(si=S1, so=S1) == ops.VQ_ERR_VALUE
+    assert _commit(acc=None) == ops.VQ_ERR_NULL
+    assert _commit(lanes=0) == ops.VQ_ERR_SHAPE
+    assert _commit(lanes=5, B=5) == ops.VQ_ERR_SHAPE
+    assert _commit(lanes=3, B=4) == ops.VQ_ERR_SHAPE
+    assert _commit(acc=A + 2) == ops.VQ_ERR_ALIGN
+    assert "lanes" in (_commit(lanes=3, B=4) and ops.last_error())
+
+
 @pytest.mark.skipif(_gpu_visible(), reason="would pass validation and launch with fake pointers")
 def test_valid_call_without_gpu_reports_device_error():
     assert _nvfp4() == ops.VQ_ERR_DEVICE
     assert ops.lib().vq_pack_fp8(A, 64, 128, A, 1 << 30, None) == ops.VQ_ERR_DEVICE
     assert ops.lib().vq_probe_copy(A, A, 1024, None) == ops.VQ_ERR_DEVICE
     assert _sample() == ops.VQ_ERR_DEVICE
+    assert _gdn(so=S0 + (6 << 20)) == ops.VQ_ERR_DEVICE  # adjacent slots do not overlap
+    assert _gdn(o=None) == ops.VQ_ERR_DEVICE
+    assert _commit() == ops.VQ_ERR_DEVICE
 
 
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
