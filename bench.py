@@ -352,6 +352,81 @@ def draft_stream(torch, ops, inputs_mod, p, steps=10):
             "gbps": round(nbytes / dt / 1e9, 1)}
 
 
+GDN_LAYERS = 48
+GDN_V_HEADS = 48
+GDN_K_HEADS = 16
+GDN_D = 128
+
+
+def gdn_bytes(layers, lanes, rows, read_q=True, write_o=True):
+    """Algorithmic bytes of the state stream: the fp32 state read from one
+    slot and written to the other, plus the rows' keys (and queries), values,
+    outputs and the two gates."""
+    n = layers * lanes
+    state = 2 * n * GDN_V_HEADS * GDN_D * GDN_D * 4
+    qk = n * rows * GDN_K_HEADS * GDN_D * 4 * (2 if read_q else 1)
+    vo = n * rows * GDN_V_HEADS * GDN_D * 4 * (2 if write_o else 1)
+    gates = n * rows * GDN_V_HEADS * 4 * 2
+    return state + qk + vo + gates
+
+
+def gdn_state_stream(torch, ops, inputs_mod, dev, steps=10, commit_rows=4):
+    """The Gated DeltaNet state stream of one verify pass: per GDN layer one
+    verify launch (the state of every lane read from one parity slot, scanned
+    over the lane's rows and written to the other slot, with the rows'
+    outputs), and after the accept scan one commit launch over all 48 layers
+    that re-scans the accepted rows from the slot the verify read (accept
+    length 4 < 8 rows, so every layer is re-scanned). Graph replays."""
+    out = {}
+    for lanes in (1, 4):
+        L, T, H, Hk = GDN_LAYERS, M_ROWS, GDN_V_HEADS, GDN_K_HEADS
+        B = L * lanes
+        state, q, k, v, a, b = inputs_mod.device_gdn_inputs((5, 7000, lanes), B, T, H, Hk, dev)
+        slot = torch.empty_like(state)
+        o = torch.empty_like(v)
+        acc = torch.full((lanes,), commit_rows, dtype=torch.int32, device=dev)
+        per_layer = [tuple(x[l * lanes:(l + 1) * lanes] for x in (state, slot, q, k, v, a, b, o)) for l in range(L)]
+
+        def verify():
+            for si, so, qq, kk, vv, aa, bb, oo in per_layer:
+                ops.vq_gdn_verify(si, so, qq, kk, vv, aa, bb, oo)
+
+        def commit():
+            ops.vq_gdn_commit(state, slot, q, k, v, a, b, acc, lanes=lanes)
+
+        res = {}
+        for name, fn in (("verify", verify), ("commit", commit)):
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(st):
+                fn()
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=st):
+                    fn()
+            torch.cuda.current_stream().wait_stream(st)
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                g.replay()
+            torch.cuda.synchronize()
+            res[name] = (time.perf_counter() - t0) / steps
+        vb = gdn_bytes(L, lanes, T)
+        cb = gdn_bytes(L, lanes, commit_rows, read_q=False, write_o=False)
+        out[str(lanes * M_ROWS)] = {
+            "lanes": lanes, "rows_per_lane": T, "state_bytes_per_slot": B * H * GDN_D * GDN_D * 4,
+            "verify_launches": L, "verify_us_per_pass": round(res["verify"] * 1e6, 1),
+            "verify_us_per_layer": round(res["verify"] * 1e6 / L, 2), "verify_bytes": vb,
+            "verify_gbps": round(vb / res["verify"] / 1e9, 1),
+            "commit_rows": commit_rows, "commit_us": round(res["commit"] * 1e6, 1), "commit_bytes": cb,
+            "commit_gbps": round(cb / res["commit"] / 1e9, 1),
+        }
+        del state, q, k, v, a, b, slot, o, per_layer
+        torch.cuda.empty_cache()
+    return out
+
+
 def sampled_verify(torch, ops, inputs_mod, p, g_steps=10, reps=20):
     """The end of the pass at nonzero temperature (temperature 1, top_k 32,
     top_p 0.95): the head also writes fp32 logits and vq_sample_accept reads
@@ -618,6 +693,8 @@ def main():
     affine = affine_q4(torch, ops, inputs, dev)
     draft = draft_stream(torch, ops, inputs, p)
     log(f"draft block: {draft['ms_per_block']:.3f} ms, {draft['gbps']:.0f} GB/s")
+    gdn = gdn_state_stream(torch, ops, inputs, dev)
+    log(f"GDN state stream at M=8: {gdn['8']}")
     log(f"affine 4-bit MLP at M=8: {affine['8']}")
     log(f"sampled verify: pass {sampled['ms_per_pass_sampled']:.3f} ms, sampler {sampled['sampler_us']:.1f} us")
     gu_w = weight_bytes("nvfp4_silu", INTER, HIDDEN)
@@ -662,6 +739,7 @@ def main():
         "sampled_verify": sampled,
         "affine_q4_mlp": affine,
         "draft_block": draft,
+        "gdn_state_stream": gdn,
         "roofline": {
             "kernel": "vq_gemm_kernel<NVFP4, SILU_MUL, M<=8> ([gate;up] 34816x5120 + SiLU*up)",
             "bound": "hbm",

@@ -20,17 +20,19 @@
 //    of one value head; its 4 waves split the 128 key rows, 32 each; within a
 //    wave lane l holds column l >> 1 and rows (l & 1) * 16 + r, r < 16, so a
 //    state load instruction reads two whole 128-byte row segments.
-//  * Per row t: u_j = sum over the lane's 16 rows, a DPP add with the lane
-//    holding the other 16 rows of that wave, then the 4 waves' sums through a
-//    double-buffered LDS slot (one barrier per row), added in wave order by
-//    every lane, so all lanes hold the same bits. Then
-//    S[i][j] = a S[i][j] + k_i * (b (v_j - a u_j)) and the output partials
-//    q^T S[:, j] go to LDS, summed in wave order after the last row.
+//  * The rows' keys, queries, values and gates are staged in LDS once, behind
+//    one barrier, so no row waits on a global load.
+//  * Per row t: u_j = the lane's 16 products (two interleaved sums), a DPP add
+//    with the lane holding the other 16 rows of that wave, then the 4 waves'
+//    sums through a double-buffered LDS slot (one barrier per row), added in
+//    wave order by every lane, so all lanes hold the same bits. Then
+//    S[i][j] = a S[i][j] + k_i * (b (v_j - a u_j)); the output partials
+//    q^T S[:, j] go to LDS and are summed in wave order after the last row.
 //  * The split of the rows over waves and lanes is fixed, so the result of a
 //    scan does not depend on how many entries a call carries: a commit
 //    re-scan of c rows is bitwise the state a verify of those c rows wrote.
 //  * The state is streamed with non-temporal loads and stores (read once and
-//    written once per pass); queries, keys, values and gates are cached.
+//    written once per pass).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,11 +42,11 @@ namespace vq {
 
 namespace {
 
-constexpr int kWaves = 4;                    // waves per workgroup (row split)
-constexpr int kRowsPerWave = kGdnDk / kWaves;  // 32
-constexpr int kRowsPerLane = kRowsPerWave / 2; // 16
-constexpr int kCols = 32;                    // state columns per workgroup
-constexpr int kChunks = kGdnDv / kCols;      // 4 workgroups per value head
+constexpr int kWaves = 4;                       // waves per workgroup (row split)
+constexpr int kRowsPerWave = kGdnDk / kWaves;   // 32
+constexpr int kRowsPerLane = kRowsPerWave / 2;  // 16
+constexpr int kCols = 32;                       // state columns per workgroup
+constexpr int kChunks = kGdnDv / kCols;         // 4 workgroups per value head
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -54,6 +56,10 @@ __device__ __forceinline__ float swap_pair(float x) {
 }
 
 __global__ __launch_bounds__(256) void gdn_scan_kernel(GdnParams p) {
+  __shared__ f32x4_t k_s[kGdnMaxT][kGdnDk / 4];
+  __shared__ f32x4_t q_s[kGdnMaxT][kGdnDk / 4];
+  __shared__ float v_s[kGdnMaxT][kCols];
+  __shared__ float a_s[kGdnMaxT], b_s[kGdnMaxT];
   __shared__ float lds_u[2][kWaves][kCols];
   __shared__ float lds_o[kGdnMaxT][kWaves][kCols];
 
@@ -63,7 +69,7 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(GdnParams p) {
   const int h = (blockIdx.x / kChunks) % p.H;
   const int e = blockIdx.x / (kChunks * p.H);
   const int kh = h / (p.H / p.Hk);
-  const int j = lane >> 1;                   // column within the chunk
+  const int j = lane >> 1;
   const int col = chunk * kCols + j;
   const int row0 = w * kRowsPerWave + (lane & 1) * kRowsPerLane;
 
@@ -75,62 +81,76 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(GdnParams p) {
     n = c < 0 ? 0 : (c > p.T ? p.T : c);
     if (n == p.T) return;  // uniform over the workgroup
   }
-
   const size_t sbase = ((size_t)e * p.H + h) * kGdnDk * kGdnDv;
   const float* sin = p.state_in + sbase + (size_t)row0 * kGdnDv + col;
   float S[kRowsPerLane];
 #pragma unroll
   for (int r = 0; r < kRowsPerLane; ++r) S[r] = __builtin_nontemporal_load(sin + (size_t)r * kGdnDv);
 
+  // stage the n rows' inputs of this head and chunk
+  const bool want_o = p.o != nullptr;
+  for (int i = threadIdx.x; i < n * (kGdnDk / 4); i += blockDim.x) {
+    const int t = i / (kGdnDk / 4), c4 = i % (kGdnDk / 4);
+    const size_t src = (((size_t)e * p.T + t) * p.Hk + kh) * kGdnDk + 4 * c4;
+    k_s[t][c4] = *reinterpret_cast<const f32x4_t*>(p.k + src);
+    if (want_o) q_s[t][c4] = *reinterpret_cast<const f32x4_t*>(p.q + src);
+  }
+  for (int i = threadIdx.x; i < n * kCols; i += blockDim.x) {
+    const int t = i / kCols, c = i % kCols;
+    v_s[t][c] = p.v[(((size_t)e * p.T + t) * p.H + h) * kGdnDv + chunk * kCols + c];
+  }
+  if (threadIdx.x < n) {
+    const size_t et = (size_t)e * p.T + threadIdx.x;
+    a_s[threadIdx.x] = p.a[et * p.H + h];
+    b_s[threadIdx.x] = p.b[et * p.H + h];
+  }
+  __syncthreads();
+
   for (int t = 0; t < n; ++t) {
-    const size_t et = (size_t)e * p.T + t;
-    const float at = p.a[et * p.H + h];
-    const float bt = p.b[et * p.H + h];
-    const float* kp = p.k + (et * p.Hk + kh) * kGdnDk + row0;
     float kr[kRowsPerLane];
 #pragma unroll
     for (int r = 0; r < kRowsPerLane; r += 4) {
-      const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(kp + r);
-      kr[r] = v4.x; kr[r + 1] = v4.y; kr[r + 2] = v4.z; kr[r + 3] = v4.w;
+      const f32x4_t k4 = k_s[t][(row0 + r) / 4];
+      kr[r] = k4.x; kr[r + 1] = k4.y; kr[r + 2] = k4.z; kr[r + 3] = k4.w;
     }
-    float u = 0.0f;
+    float u0 = 0.0f, u1 = 0.0f;
 #pragma unroll
-    for (int r = 0; r < kRowsPerLane; ++r) u = __builtin_fmaf(kr[r], S[r], u);
+    for (int r = 0; r < kRowsPerLane; r += 2) {
+      u0 = __builtin_fmaf(kr[r], S[r], u0);
+      u1 = __builtin_fmaf(kr[r + 1], S[r + 1], u1);
+    }
+    float u = u0 + u1;
     u += swap_pair(u);
     if ((lane & 1) == 0) lds_u[t & 1][w][j] = u;
     __syncthreads();
     u = lds_u[t & 1][0][j];
 #pragma unroll
     for (int w2 = 1; w2 < kWaves; ++w2) u += lds_u[t & 1][w2][j];
-
-    const float vj = p.v[(et * p.H + h) * kGdnDv + col];
-    const float wj = bt * (vj - at * u);
+    const float at = a_s[t];
+    const float wj = b_s[t] * (v_s[t][j] - at * u);
 #pragma unroll
     for (int r = 0; r < kRowsPerLane; ++r) S[r] = __builtin_fmaf(kr[r], wj, at * S[r]);
-
-    if (p.o) {
-      const float* qp = p.q + (et * p.Hk + kh) * kGdnDk + row0;
-      float op = 0.0f;
+    if (want_o) {
+      float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
       for (int r = 0; r < kRowsPerLane; r += 4) {
-        const f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(qp + r);
-        op = __builtin_fmaf(q4.x, S[r], op);
-        op = __builtin_fmaf(q4.y, S[r + 1], op);
-        op = __builtin_fmaf(q4.z, S[r + 2], op);
-        op = __builtin_fmaf(q4.w, S[r + 3], op);
+        const f32x4_t q4 = q_s[t][(row0 + r) / 4];
+        o0 = __builtin_fmaf(q4.x, S[r], o0);
+        o1 = __builtin_fmaf(q4.y, S[r + 1], o1);
+        o0 = __builtin_fmaf(q4.z, S[r + 2], o0);
+        o1 = __builtin_fmaf(q4.w, S[r + 3], o1);
       }
+      float op = o0 + o1;
       op += swap_pair(op);
       if ((lane & 1) == 0) lds_o[t][w][j] = op;
     }
   }
-
   float* sout = p.state_out + sbase + (size_t)row0 * kGdnDv + col;
 #pragma unroll
   for (int r = 0; r < kRowsPerLane; ++r) __builtin_nontemporal_store(S[r], sout + (size_t)r * kGdnDv);
-
-  if (p.o && n > 0) {
+  if (want_o && n > 0) {
     __syncthreads();
-    // one thread per (row t, column): the wave partials in wave order
+    // one thread per (row, column): the wave partials in wave order
     for (int idx = threadIdx.x; idx < n * kCols; idx += blockDim.x) {
       const int t = idx / kCols, jj = idx % kCols;
       float s = lds_o[t][0][jj];
