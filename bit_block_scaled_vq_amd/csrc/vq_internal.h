@@ -1,5 +1,7 @@
 // Internal interface between the C-ABI layer (libverify.cpp) and the HIP
-// kernels (vq_kernels.hip). Not installed; not part of the public ABI.
+// kernels (vq_kernels.hip: GEMMs, packing, probes; vq_sample.hip: sampled
+// verify; vq_gdn.hip: GDN state stream). Not installed; not part of the
+// public ABI.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>

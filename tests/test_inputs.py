@@ -58,3 +58,15 @@ def test_drafts_follow_argmax_with_p():
     d = inputs.drafts((7,), a, 10**9)
     assert d.dtype == np.int32 and d.shape == (5000, 7)
     assert abs((d == a[:, :7]).mean() - 0.7) < 0.01
+
+
+def test_gdn_inputs_recipe():
+    st, q, k, v, a, b = inputs.gdn_inputs((3,), 2, 8, 6, 2)
+    st2, *_ = inputs.gdn_inputs((3,), 2, 8, 6, 2)
+    assert np.array_equal(st, st2)
+    assert st.shape == (2, 6, 128, 128) and q.shape == k.shape == (2, 8, 2, 128) and v.shape == (2, 8, 6, 128)
+    assert all(x.dtype == np.float32 for x in (st, q, k, v, a, b))
+    assert np.allclose(np.linalg.norm(q.astype(np.float64), axis=-1), 1, atol=1e-6)
+    assert np.allclose(np.linalg.norm(k.astype(np.float64), axis=-1), 1, atol=1e-6)
+    assert (a > 0).all() and (a <= 1).all() and (b > 0).all() and (b < 1).all()
+    assert abs(st.std() - 0.05) < 0.002 and abs(v.std() - 1) < 0.05
