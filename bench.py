@@ -427,6 +427,53 @@ def gdn_state_stream(torch, ops, inputs_mod, dev, steps=10, commit_rows=4):
     return out
 
 
+def pass_with_state(torch, ops, inputs_mod, p, steps=10):
+    """The verify pass with its Gated DeltaNet state stream in model order:
+    each GDN layer's state step runs between its in- and out-projection, and
+    after the head the commit re-scans the accepted rows of every GDN layer,
+    its count read on the device from the head's accept length (no host
+    round trip). One graph, replayed."""
+    dev = p.dev
+    L, T, H, Hk = GDN_LAYERS, M_ROWS, GDN_V_HEADS, GDN_K_HEADS
+    state, q, k, v, a, b = inputs_mod.device_gdn_inputs((5, 7100), L, T, H, Hk, dev)
+    slot = torch.empty_like(state)
+    o = torch.empty_like(v)
+    per_layer = [tuple(x[l:l + 1] for x in (state, slot, q, k, v, a, b, o)) for l in range(L)]
+
+    def run():
+        layer = 0
+        for i, item in enumerate(p.items):
+            p.launch(i)
+            if item[0] == "gdn_in":
+                ops.vq_gdn_verify(*per_layer[layer])
+                layer += 1
+        ops.vq_gdn_commit(state, slot, q, k, v, a, b, p.accept, lanes=1)
+
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        run()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            run()
+    torch.cuda.current_stream().wait_stream(st)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    acc = int(p.accept.item())
+    state_b = gdn_bytes(L, 1, T) + (gdn_bytes(L, 1, acc, read_q=False, write_o=False) if acc < T else 0)
+    del state, q, k, v, a, b, slot, o, per_layer
+    torch.cuda.empty_cache()
+    return {"ms_per_pass": round(dt * 1e3, 4), "launches": len(p.items) + L + 1, "accept_len": acc,
+            "weight_bytes": p.weight_bytes, "state_stream_bytes": state_b,
+            "gbps": round((p.weight_bytes + state_b) / dt / 1e9, 1)}
+
+
 def sampled_verify(torch, ops, inputs_mod, p, g_steps=10, reps=20):
     """The end of the pass at nonzero temperature (temperature 1, top_k 32,
     top_p 0.95): the head also writes fp32 logits and vq_sample_accept reads
@@ -695,6 +742,8 @@ def main():
     log(f"draft block: {draft['ms_per_block']:.3f} ms, {draft['gbps']:.0f} GB/s")
     gdn = gdn_state_stream(torch, ops, inputs, dev)
     log(f"GDN state stream at M=8: {gdn['8']}")
+    with_state = pass_with_state(torch, ops, inputs, p)
+    log(f"pass with the GDN state stream: {with_state}")
     log(f"affine 4-bit MLP at M=8: {affine['8']}")
     log(f"sampled verify: pass {sampled['ms_per_pass_sampled']:.3f} ms, sampler {sampled['sampler_us']:.1f} us")
     gu_w = weight_bytes("nvfp4_silu", INTER, HIDDEN)
@@ -740,6 +789,7 @@ def main():
         "affine_q4_mlp": affine,
         "draft_block": draft,
         "gdn_state_stream": gdn,
+        "pass_with_gdn_state": with_state,
         "roofline": {
             "kernel": "vq_gemm_kernel<NVFP4, SILU_MUL, M<=8> ([gate;up] 34816x5120 + SiLU*up)",
             "bound": "hbm",
