@@ -602,10 +602,20 @@ def cpu_baseline(inputs_mod, budget_s=20.0):
     b_f4 = sum(weight_bytes(f, n, k) for _, f, n, k in items if f != "fp8")
     b_f8 = sum(weight_bytes(f, n, k) for _, f, n, k in items if f == "fp8")
     s_pass = b_f4 / (gbps_f4 * 1e9) + b_f8 / (gbps_f8 * 1e9)
+    # the GDN state stream's oracle: one layer's verify scan (48 value heads,
+    # 16 key heads, 8 rows), scaled to the 48 GDN layers of a pass
+    gin = inputs_mod.gdn_inputs((6, 3), 1, M_ROWS, GDN_V_HEADS, GDN_K_HEADS)
+    t0 = time.perf_counter()
+    O.gdn_scan(*gin)
+    t_gdn = time.perf_counter() - t0
+    gdn = {"ms_per_pass": round(t_gdn * GDN_LAYERS * 1e3, 1),
+           "gbps": round(gdn_bytes(1, 1, M_ROWS) / t_gdn / 1e9, 4),
+           "sample": "fp64 numpy oracle, one layer's verify scan (48 heads x 8 rows), x48 layers"}
     return {
         "value": round((b_f4 + b_f8) / s_pass / 1e9, 4),
         "unit": "GB/s",
         "ms_per_pass": round(s_pass * 1e3, 1),
+        "gdn_state_stream": gdn,
         "cores": int(cores),
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle, M=8: {n_f4}x NVFP4 4096x5120 and {n_f8}x FP8 4096x5120 row slices "
