@@ -87,22 +87,55 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(GdnParams p) {
 #pragma unroll
   for (int r = 0; r < kRowsPerLane; ++r) S[r] = __builtin_nontemporal_load(sin + (size_t)r * kGdnDv);
 
-  // stage the n rows' inputs of this head and chunk
+  // stage the n rows' inputs of this head and chunk: every global load is
+  // issued before the first LDS write, so staging costs one round trip (and
+  // overlaps the state loads above)
   const bool want_o = p.o != nullptr;
-  for (int i = threadIdx.x; i < n * (kGdnDk / 4); i += blockDim.x) {
-    const int t = i / (kGdnDk / 4), c4 = i % (kGdnDk / 4);
-    const size_t src = (((size_t)e * p.T + t) * p.Hk + kh) * kGdnDk + 4 * c4;
-    k_s[t][c4] = *reinterpret_cast<const f32x4_t*>(p.k + src);
-    if (want_o) q_s[t][c4] = *reinterpret_cast<const f32x4_t*>(p.q + src);
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kQKSlots = kGdnMaxT * (kGdnDk / 4) / kThreads;  // float4s per thread
+  constexpr int kVSlots = kGdnMaxT * kCols / kThreads;          // values per thread
+  f32x4_t kreg[kQKSlots], qreg[kQKSlots];
+  float vreg[kVSlots];
+  float areg = 0.0f, breg = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kQKSlots; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    if (i < n * (kGdnDk / 4)) {
+      const int t = i / (kGdnDk / 4), c4 = i % (kGdnDk / 4);
+      const size_t src = (((size_t)e * p.T + t) * p.Hk + kh) * kGdnDk + 4 * c4;
+      kreg[u] = *reinterpret_cast<const f32x4_t*>(p.k + src);
+      if (want_o) qreg[u] = *reinterpret_cast<const f32x4_t*>(p.q + src);
+    }
   }
-  for (int i = threadIdx.x; i < n * kCols; i += blockDim.x) {
-    const int t = i / kCols, c = i % kCols;
-    v_s[t][c] = p.v[(((size_t)e * p.T + t) * p.H + h) * kGdnDv + chunk * kCols + c];
+#pragma unroll
+  for (int u = 0; u < kVSlots; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    if (i < n * kCols) {
+      const int t = i / kCols, c = i % kCols;
+      vreg[u] = p.v[(((size_t)e * p.T + t) * p.H + h) * kGdnDv + chunk * kCols + c];
+    }
   }
   if (threadIdx.x < n) {
     const size_t et = (size_t)e * p.T + threadIdx.x;
-    a_s[threadIdx.x] = p.a[et * p.H + h];
-    b_s[threadIdx.x] = p.b[et * p.H + h];
+    areg = p.a[et * p.H + h];
+    breg = p.b[et * p.H + h];
+  }
+#pragma unroll
+  for (int u = 0; u < kQKSlots; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    if (i < n * (kGdnDk / 4)) {
+      k_s[i / (kGdnDk / 4)][i % (kGdnDk / 4)] = kreg[u];
+      if (want_o) q_s[i / (kGdnDk / 4)][i % (kGdnDk / 4)] = qreg[u];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kVSlots; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    if (i < n * kCols) v_s[i / kCols][i % kCols] = vreg[u];
+  }
+  if (threadIdx.x < n) {
+    a_s[threadIdx.x] = areg;
+    b_s[threadIdx.x] = breg;
   }
   __syncthreads();
 
