@@ -293,7 +293,8 @@ int32_t vq_sample_accept(const float* logits, int32_t lanes, int32_t R, int32_t 
  *   q, k       fp32 [B][T][Hk][128], 16-byte aligned
  *   v          fp32 [B][T][H][128]
  *   a, b       fp32 [B][T][H]: decay and write strength of each row and head
- *   o          fp32 [B][T][H][128] or NULL: the output of every row
+ *   o          fp32 [B][T][H][128] or NULL: the output of every row; must
+ *              not overlap any other array of the call
  * Shapes: 1 <= B, 1 <= T <= 16, 1 <= Hk <= H, H % Hk == 0, B * H <= 2^24.
  * All arrays 4-byte aligned (q, k 16-byte). One launch on `stream`, no
  * workspace; fp32 arithmetic with every sum in a fixed order, and the row
