@@ -196,3 +196,38 @@ def test_gdn_graph_replay_matches_eager():
         assert torch.equal(y, eager_s) and torch.equal(o, eager_o), i
         ops.vq_gdn_verify(state, ye, q, k, v, a, b, oe)
         torch.cuda.synchronize()
+
+
+def test_head_accept_length_drives_the_commit_on_device():
+    # the accept lengths the vocabulary head writes on the device are the
+    # counts the GDN commit reads: the two calls chain with no host round
+    # trip, and the committed state equals the oracle's commit at the
+    # oracle's accept lengths (seeded inputs without tie-class rows)
+    from tests.gpu_helpers import to_dev_bf16, to_dev_u8
+    torch, dev = torch_dev()
+    ops = _ops()
+    lanes, R, V, K = 2, 8, 4096, 512
+    M = lanes * R
+    hb = inputs.x_bf16((710,), M, K)
+    codes, scales = inputs.nvfp4_weights((710,), V, K)
+    logits = O.gemm_nvfp4(hb, codes, scales, 1.0)
+    assert O.top2_gap(logits).min() > 1e-3
+    am = O.argmax_lowest(logits).reshape(lanes, R)
+    dr = inputs.drafts((710,), am, V)
+    acc_ref, _ = O.greedy_accept(am, dr)
+    w = ops.pack_nvfp4(to_dev_u8(codes), to_dev_u8(scales))
+    am_d = torch.empty(M, dtype=torch.int32, device=dev)
+    acc_d = torch.full((lanes,), -7, dtype=torch.int32, device=dev)
+    layers, T, H, Hk = 3, R, 6, 2
+    host = inputs.gdn_inputs((711,), layers * lanes, T, H, Hk)
+    state, q, k, v, a, b = _dev(host)
+    slot = torch.empty_like(state)
+    ops.vq_gdn_verify(state, slot, q, k, v, a, b)
+    ops.vq_lmhead_argmax_accept(to_dev_bf16(hb), w, 1.0, V, torch.from_numpy(dr).to(dev), lanes, R, am_d, acc_d,
+                                workspace=ops.workspace(ops.VQ_OP_LMHEAD, M, V, K, dev))
+    ops.vq_gdn_commit(state, slot, q, k, v, a, b, acc_d, lanes=lanes)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc_d.cpu().numpy(), acc_ref), (acc_d.cpu().numpy(), acc_ref)
+    st_ref, _ = O.gdn_scan(*host)
+    want = O.gdn_commit(host[0], st_ref, *host[1:], acc_ref, lanes)
+    _check(slot.cpu().numpy(), want, T, "commit driven by the head's accept lengths")
