@@ -231,3 +231,49 @@ def test_head_accept_length_drives_the_commit_on_device():
     st_ref, _ = O.gdn_scan(*host)
     want = O.gdn_commit(host[0], st_ref, *host[1:], acc_ref, lanes)
     _check(slot.cpu().numpy(), want, T, "commit driven by the head's accept lengths")
+
+
+def _min_decision_margin(z, u, t, k, tp):
+    # fp64 margins of the top_p cut and of the inverse-CDF draw per row
+    out = np.inf
+    for r in range(z.shape[0]):
+        ids = O.candidate_order(z[r])[:k]
+        w = np.exp((z[r][ids].astype(np.float64) - z[r][ids[0]]) / t)
+        out = min(out, float(np.min(np.abs(np.cumsum(w) / w.sum() - tp))))
+        _, p = O.target_distribution(z[r], t, k, tp)
+        if len(p) > 1:
+            out = min(out, float(np.min(np.abs(np.cumsum(p)[:-1] - u[r]))))
+    return out
+
+
+def test_sampled_accept_length_drives_the_commit_on_device():
+    # the point-mass sampled verify writes its accept lengths on the device and
+    # the GDN commit reads them: lane 0 keeps 4 rows (re-scanned), lane 1 all 8
+    # (its slot is kept); seeded inputs whose decisions all clear the fp32/fp64
+    # tie margin, so the accept lengths are exact
+    torch, dev = torch_dev()
+    ops = _ops()
+    lanes, R, V = 2, 8, 8192
+    M = lanes * R
+    z = inputs.logits_f32((712,), M, V)
+    u = inputs.uniforms((712,), M)
+    assert _min_decision_margin(z, u, 1.0, 32, 0.95) > 1e-5
+    toks = O.row_draws(z, 1.0, 32, 0.95, u).reshape(lanes, R)
+    dr = toks[:, :R - 1].copy().astype(np.int32)
+    dr[0, 3] = (dr[0, 3] + 1) % V
+    acc_ref, _ = O.point_mass_accept(toks, dr)
+    assert list(acc_ref) == [4, 8]
+    layers, T, H, Hk = 2, R, 6, 2
+    host = inputs.gdn_inputs((713,), layers * lanes, T, H, Hk)
+    state, q, k, v, a, b = _dev(host)
+    slot = torch.empty_like(state)
+    ops.vq_gdn_verify(state, slot, q, k, v, a, b)
+    acc_d = torch.full((lanes,), -7, dtype=torch.int32, device=dev)
+    ops.vq_sample_accept(torch.from_numpy(z).to(dev), lanes, R, 1.0, 32, 0.95, torch.from_numpy(u).to(dev), acc_d,
+                         draft=torch.from_numpy(dr).to(dev), workspace=ops.workspace(ops.VQ_OP_SAMPLE, M, V, 0, dev))
+    ops.vq_gdn_commit(state, slot, q, k, v, a, b, acc_d, lanes=lanes)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc_d.cpu().numpy(), acc_ref)
+    st_ref, _ = O.gdn_scan(*host)
+    want = O.gdn_commit(host[0], st_ref, *host[1:], acc_ref, lanes)
+    _check(slot.cpu().numpy(), want, T, "commit driven by the sampled accept lengths")
