@@ -682,6 +682,36 @@ def pmc_workload(m_rows=M_ROWS, copies=4, reps=2):
                                        "gate_up_activation_bytes": act_bytes(INTER, HIDDEN, m_rows)}}), flush=True)
 
 
+def pmc_gdn_workload(reps=2, commit_rows=4):
+    """Hardware-counter workload of the GDN state stream: the copy probe on
+    1 GiB (calibration), then the commit over 48 layers x 1 lane (accept
+    length 4 of 8 rows, so every layer is re-scanned: the state read from one
+    slot and written to the other) and one per-layer verify launch."""
+    import torch
+    from bit_block_scaled_vq_amd import inputs, ops
+    dev = torch.device("cuda:0")
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    for _ in range(reps):
+        ops.vq_probe_copy(src, dst)
+    torch.cuda.synchronize()
+    del src, dst
+    L, T, H, Hk = GDN_LAYERS, M_ROWS, GDN_V_HEADS, GDN_K_HEADS
+    state, q, k, v, a, b = inputs.device_gdn_inputs((5, 7200), L, T, H, Hk, dev)
+    slot = torch.empty_like(state)
+    o = torch.empty_like(v)
+    acc = torch.full((1,), commit_rows, dtype=torch.int32, device=dev)
+    for _ in range(reps):
+        ops.vq_gdn_commit(state, slot, q, k, v, a, b, acc, lanes=1)
+    ops.vq_gdn_verify(state[:1], slot[:1], q[:1], k[:1], v[:1], a[:1], b[:1], o[:1])
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_gdn_workload": {"copy_probe_bytes_each": nbytes, "copy_probe_launches": reps,
+                                           "commit_launches": reps, "commit_rows": commit_rows,
+                                           "commit_bytes": gdn_bytes(L, 1, commit_rows, read_q=False, write_o=False),
+                                           "verify_launches": 1, "verify_bytes": gdn_bytes(1, 1, T)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -692,9 +722,14 @@ def main():
     ap.add_argument("--pmc-workload", action="store_true",
                     help="run only the small hardware-counter workload (copy probe + dominant kernel)")
     ap.add_argument("--pmc-rows", type=int, default=M_ROWS, help="activation rows M of the counter workload")
+    ap.add_argument("--pmc-gdn-workload", action="store_true",
+                    help="run only the hardware-counter workload of the GDN state stream (copy probe + commit)")
     args = ap.parse_args()
     if args.pmc_workload:
         pmc_workload(args.pmc_rows)
+        return
+    if args.pmc_gdn_workload:
+        pmc_gdn_workload()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the verify-pass weight stream is built and timed on a single "
