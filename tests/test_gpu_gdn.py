@@ -44,7 +44,8 @@ def _check(gpu, ref, T, what):
     assert e <= gdn_tol(T), (what, e)
 
 
-@pytest.mark.parametrize("B,T,H,Hk", [(1, 8, 48, 16), (2, 1, 4, 4), (3, 5, 6, 2), (4, 16, 3, 1), (2, 8, 2, 1)])
+@pytest.mark.parametrize("B,T,H,Hk", [(1, 8, 48, 16), (2, 1, 4, 4), (3, 5, 6, 2), (4, 16, 3, 1), (2, 8, 2, 1),
+                                      (4, 16, 48, 16)])
 def test_gdn_verify_matches_oracle(B, T, H, Hk):
     say(f"case: gdn verify B={B} T={T} H={H} Hk={Hk}")
     torch, dev = torch_dev()
