@@ -16,8 +16,8 @@ Sources (page titles and sections):
        has probability zero) and section "What is actually open" (the check is
        distribution equivalence at temperature 1, top_k 32).
   [P2] "Beating Splash on an M5 Max": section "What actually moved the
-       needle" (one GPU kernel over the verify logits applies top-k and top-p,
-       samples, runs the acceptance rule and writes a small result block).
+       needle" (the sampler's truncation, its draw and the accept test all
+       run on the GPU, which hands back only a compact result block).
   [P3] "Speculative decoding": section "Is it really lossless?" (with
        sampling, accepted drafts plus the resampled correction are an exact
        sample of the target).

@@ -102,3 +102,35 @@ def test_nine_bytes_per_sixteen():
     # 32 B of nibbles + 2 B scale + 2 B bias per 64 weights
     assert (32 + 2 + 2) * 16 == 64 * 9
     assert O.AFFINE_GROUP == 64
+
+
+def test_mlp_silu_mul_affine_fused_split():
+    # silu(gate) * up on the fused [gate; up] matrix: rows [0, inter) are the
+    # gate, rows [inter, 2 inter) the up projection of the same output column.
+    # Each product is brute-forced from exact rationals (the bf16 fields decoded
+    # through torch), so swapping the halves, dropping the SiLU or reading the
+    # wrong row fails here, and h's single bf16 rounding is torch's cast.
+    import math
+    inter, k, m = 6, 128, 3
+    codes, sb, bb = _rand_affine(7, 2 * inter, k)
+    x = _bf16_bits(np.random.default_rng(8).standard_normal((m, k)).astype(np.float32))
+    h, hb = O.mlp_silu_mul_affine(x, codes, sb, bb, inter)
+    assert h.shape == (m, inter) and hb.shape == (m, inter)
+
+    def dot(i, row):
+        xf = [_bf16_fraction(x[i, t]) for t in range(k)]
+        return sum(xf[t] * (_bf16_fraction(sb[row, t // 64]) * _q(codes, row, t) + _bf16_fraction(bb[row, t // 64]))
+                   for t in range(k))
+
+    asym = 0
+    for i in range(m):
+        for j in range(inter):
+            g = float(dot(i, j))
+            u = float(dot(i, inter + j))
+            ref = g / (1.0 + math.exp(-g)) * u
+            assert abs(h[i, j] - ref) <= 1e-12 * max(1.0, abs(ref)), (i, j)
+            swapped = u / (1.0 + math.exp(-u)) * g
+            asym += abs(swapped - ref) > 1e-6 * max(1.0, abs(ref))
+    assert asym > 0   # the inputs tell gate and up apart
+    want = torch.from_numpy(h.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(hb, want)
