@@ -157,7 +157,8 @@ def workspace_bytes(op: int, M: int, N: int, K: int) -> int:
 
 
 def workspace(op: int, M: int, N: int, K: int, device="cuda"):
-    """A zero-filled workspace for `op` (reusable across stream-ordered calls)."""
+    """A zero-filled workspace for `op` at (N, K): bound to that (op, N, K),
+    reusable by any number of stream-ordered calls of it at any M."""
     torch = _torch()
     n = workspace_bytes(op, M, N, K)
     if n == 0:

@@ -55,11 +55,18 @@
  *     arrays 4-byte aligned; the workspace 16-byte aligned. A packed size
  *     (w_bytes) smaller than the shape needs returns VQ_ERR_SHAPE.
  *   - workspace: device memory of at least vq_workspace_bytes(op, M, N, K)
- *     bytes, zero-filled by the caller ONCE before its first use. Kernels leave
- *     every counter in it at zero again, so one workspace can be reused by
- *     any number of stream-ordered calls (and graph replays). Two calls that
- *     may run concurrently need distinct workspaces. A NULL or short workspace
- *     returns VQ_ERR_WORKSPACE; the schedule never changes silently.
+ *     bytes, zero-filled by the caller ONCE before its first use. A workspace
+ *     is BOUND to one (op, N, K): its layout (partial-sum slots, per-tile
+ *     counters, argmax buckets, done counter) is placed from those three
+ *     values, and a call with another op, N or K would find its counters on
+ *     the previous shape's non-zero partial sums. Within that binding it
+ *     serves every M (the size and layout do not depend on M). Kernels leave
+ *     every counter in it at zero again, so a bound workspace can be reused
+ *     by any number of stream-ordered calls (and graph replays); reusing it
+ *     for another (op, N, K) requires zero-filling it again first. Two calls
+ *     that may run concurrently need distinct workspaces. A NULL or short
+ *     workspace returns VQ_ERR_WORKSPACE; the schedule never changes
+ *     silently.
  *   - Results are deterministic: the K partition and the order of the fixed
  *     split-K reduction depend only on (N, K) and the epilogue, never on M.
  *     FP8 and affine 4-bit: row r of an M-row call equals row r of any other
@@ -323,8 +330,10 @@ int32_t vq_gdn_commit(const float* state_in, float* state_out, const float* q, c
 /* Workspace bytes needed by `op` at this shape (for VQ_OP_NVFP4_SILU_MUL, N is
  * the output width, i.e. half the weight rows; for VQ_OP_LMHEAD, N = V and
  * M = lanes * R). Returns 0 for an invalid shape. The size does not depend
- * on M beyond the M <= 32 bound, so one workspace serves every M; for
- * VQ_OP_SAMPLE, N = V, K is ignored and the size grows with M. */
+ * on M beyond the M <= 32 bound, so a workspace bound to one (op, N, K)
+ * serves every M; for VQ_OP_SAMPLE, N = V, K is ignored, the size grows
+ * with M, and the per-lane counters sit at an offset placed from (M, V), so a
+ * sampling workspace is bound to one (M, V). */
 size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K);
 
 const char* vq_status_str(int32_t status);
