@@ -41,7 +41,8 @@
 //    from MFMAs against ones, and s * (x . (128+q)) + (b - 128 s) * sum(x) is
 //    accumulated in fp32.
 //  * Weights stream with non-temporal 16-byte loads, 3 iterations in flight
-//    per wave.
+//    per wave; one workgroup of 4 waves per CU, registers budgeted for one
+//    wave per SIMD.
 //  * Stream-K over 4-wave workgroups: workgroup g owns iterations
 //    [g*W/G, (g+1)*W/G) of the (tile, iteration) space and each wave a
 //    contiguous quarter of that. Tiles shared by waves of one workgroup are
@@ -424,21 +425,26 @@ struct Acc {
 template <int FMT, int RG>
 __device__ __forceinline__ void compute_iter(const WBuf<FMT>& b, const XBuf<RG>& x, Acc<FMT, RG>& acc) {
   if constexpr (FMT == FMT_NVFP4) {
+    // All 16 MFMAs of the block first, each into its own result registers,
+    // then the block-scale FMAs: the matrix unit's latency is covered by the
+    // other MFMAs and the decodes instead of stalling every FMA chain (the
+    // summation order per accumulator is unchanged: j = 0..3 within t).
+    static_assert(RG == 1, "the block-scale-after-MFMA family serves M <= 8 (one row group)");
+    f32x4_t d[kNT][4];
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
+    for (int t = 0; t < kNT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        d[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[0][j]),
+                                                          dec_fp4x8(b.c[t][j]), f32x4_t{}, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < kNT; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8_t wv = dec_fp4x8(b.c[t][j]);
         const float sc = scale_byte(b.s[t], j);
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-          const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[rg][j]), wv,
-                                                                    f32x4_t{}, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc.v[t][4 * rg + r] = __builtin_fmaf(sc, d[r], acc.v[t][4 * rg + r]);
-        }
+        for (int r = 0; r < 4; ++r) acc.v[t][r] = __builtin_fmaf(sc, d[t][j][r], acc.v[t][r]);
       }
-    }
   } else if constexpr (FMT == FMT_NVFP4S) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
@@ -611,10 +617,26 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int tile, int lane
 }
 
 // Cross-workgroup data (partial sums, counters, argmax candidates) only moves
-// through agent-scope atomics: relaxed atomic stores and loads are coherent at
-// device scope, so waiting for the stores' acknowledgement before the counter
-// increment orders them, and no L2 write-back or invalidate is needed.
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+// through agent-scope atomics, which gfx950 performs with the SC1 bit: stores
+// write through to the memory side (the level all eight XCDs share) and loads
+// and read-modify-writes are served there, so they are coherent across XCDs
+// without any L2 write-back or invalidate. The ordering a piece needs --
+// "every store of my piece is visible before my counter increment" -- comes
+// from s_waitcnt vmcnt(0): on gfx9 a vector store decrements vmcnt only when
+// the memory system acknowledges it, and an SC1 store is acknowledged once it
+// is written at that shared level. So after the wait, any agent that observes
+// the increment and then issues SC1 loads sees the piece. The reader side
+// needs no wait of its own: its loads are issued after the counter value they
+// depend on has returned. The compiler does not model s_waitcnt as touching
+// memory, so compiler-only fences on both sides keep it from moving the atomic
+// stores or the counter operation across the wait (no instruction is emitted
+// for them). The formally ordered alternative -- a release on the counter
+// increment -- costs an L2 write-back (buffer_wbl2) per piece.
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Stream-K over workgroups: workgroup g owns iterations [g*W/G, (g+1)*W/G).
 __device__ __forceinline__ int64_t wg_start(int64_t g, const GemmParams& p) { return g * p.total / p.wgs; }
@@ -667,6 +689,7 @@ __device__ __forceinline__ bool arrive(const GemmParams& p, int tile, int lane) 
   uint32_t old = 0;
   if (lane == 0) old = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the pieces' loads stay after the counter value
   const int64_t t0 = (int64_t)tile * p.iters;
   return old == (uint32_t)(wg_of(t0 + p.iters - 1, p) - wg_of(t0, p));
 }
@@ -725,11 +748,14 @@ struct PipeDepth {
   // trades ring depth for a second wave per SIMD (measured faster)
   static constexpr int value = (FMT == FMT_NVFP4S && RG == 2) ? 2 : (RG <= 2 ? 3 : 2);
 };
-// Waves per SIMD: one row group keeps two waves per SIMD; more row groups keep
-// one wave per SIMD so the extra accumulators and X fragments stay in registers.
+// Workgroups per CU the register budget is sized for. Every launch has at
+// most one workgroup per CU (at most 256 workgroups of 4 waves), so one wave
+// per SIMD is all that ever runs: the bound only lets the compiler keep the
+// MFMA results, the prefetch ring and the accumulators in registers (measured
+// 2 % faster over the pass than budgeting for two waves per SIMD).
 template <int FMT, int RG>
 struct Occupancy {
-  static constexpr int value = (RG == 1 || (FMT == FMT_NVFP4S && RG == 2)) ? 2 : 1;
+  static constexpr int value = 1;
 };
 
 // Schedule. Workgroup g (4 waves) owns the iteration range [S, E) of the
@@ -902,6 +928,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
       uint32_t old = 0;
       if (lane == 0) old = __hip_atomic_fetch_add(p.done, (uint32_t)finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       old = __shfl(old, 0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // head_final's bucket loads stay after the count
       if (old + (uint32_t)finished == (uint32_t)p.tiles) head_final(p, lane);
     }
   }
@@ -946,12 +973,8 @@ static int launch_rg(const GemmParams& p, hipStream_t st) {
   const int rg = (p.M + rows - 1) / rows;
   const dim3 grid((unsigned)p.wgs), block(256);
   if constexpr (FMT == FMT_NVFP4) {
-    switch (rg) {
-      case 1: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p); break;
-      case 2: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p); break;
-      case 3: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 3>), grid, block, 0, st, p); break;
-      default: hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 4>), grid, block, 0, st, p); break;
-    }
+    (void)rg;  // launch_gemm sends M > 8 to the scaled family
+    hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p);
   } else {
     if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p);

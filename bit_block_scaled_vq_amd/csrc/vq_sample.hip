@@ -365,11 +365,19 @@ __global__ __launch_bounds__(256) void sample_row_kernel(SampleParams p) {
     __hip_atomic_store(&p.row_meta[2 * m], count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&p.row_meta[2 * m + 1], tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // The agent-scope (SC1) stores above are acknowledged by the shared memory
+  // level before vmcnt drops, so after this wait the row is visible to any
+  // agent that sees the count below; compiler-only fences keep the compiler
+  // from moving the stores or the count across the wait (s_waitcnt is not
+  // modelled as a memory operation).
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   const int l = m / p.R;
   uint32_t old = 0;
   if (lane == 0) old = __hip_atomic_fetch_add(&p.lane_count[l], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // lane_scan's loads stay after the count
   if (old != (uint32_t)(p.R - 1)) return;
   lane_scan(p, l, lane);
   if (lane == 0) __hip_atomic_store(&p.lane_count[l], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

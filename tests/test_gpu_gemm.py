@@ -328,3 +328,44 @@ def test_mlp_gate_up_full_size_wide_rows(m):
     r = run_nvfp4(x, gu_c, gu_s, 1.0, inter, epi=1)
     check_f32(r["f32"], h_ref, what=f"h M{m}")
     check_bf16_store(r["bf16"], r["f32"], h_ref)
+
+
+# ----------------------------------------- every E4M3 block-scale code, both families
+
+def _all_scale_codes_case(m):
+    """K = 128 (8 scale blocks per row), 32 weight rows: the 32 x 8 block
+    scales take every finite E4M3FN code once (0x00-0x7E and 0x80-0xFE, 254
+    codes, two repeated) and every code nibble is non-zero, so each scale's
+    decode reaches the output. Activation row i is one-hot at k = 16 (i % 8)
+    + 2 (i // 8) + 1: rows 0-7 hit the 8 scale blocks, rows 8-15 the same
+    blocks at other k. Y[i, n] = E2M1(code[n, k_i]) * E4M3(scale[n, k_i / 16])
+    * ts exactly (every such product is exact in bf16 and fp32)."""
+    n, k, ts = 32, 128, 0.75
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    scales = np.concatenate([finite, finite[:2]]).reshape(n, k // 16)
+    g = np.random.default_rng(1234)
+    lo = g.integers(1, 16, size=(n, k // 2), dtype=np.uint8)
+    hi = g.integers(1, 16, size=(n, k // 2), dtype=np.uint8)
+    lo[lo == 8] = 9  # 8 is -0
+    hi[hi == 8] = 9
+    codes = (lo | (hi << 4)).astype(np.uint8)
+    ks = [16 * (i % 8) + 2 * (i // 8) + 1 for i in range(m)]
+    x = np.zeros((m, k), dtype=np.uint16)
+    for i, kk in enumerate(ks):
+        x[i, kk] = 0x3F80
+    w = O.dequant_nvfp4(codes, scales, ts)
+    want = np.stack([w[:, kk] for kk in ks]).astype(np.float32).astype(np.float64)
+    return x, codes, scales, ts, n, want
+
+
+@pytest.mark.parametrize("m", [8, 16])
+def test_nvfp4_every_block_scale_code_bit_exact(m):
+    # m = 8: the block-scale-after-MFMA family; m = 16: weights scaled in registers
+    say(f"case: every finite E4M3 block-scale code, one-hot activations, M={m}")
+    x, codes, scales, ts, n, want = _all_scale_codes_case(m)
+    r = run_nvfp4(x, codes, scales, ts, n, out="f32")
+    got = r["f32"].astype(np.float64)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:8]
+    # the decoded scales span the whole E4M3FN range, subnormals included
+    used = O.E4M3FN_TABLE[scales]
+    assert np.nanmax(used) == 448.0 and np.min(np.abs(used[used != 0])) == 2.0 ** -9
