@@ -311,6 +311,52 @@ int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* w, size_t w_bytes, float
   return launch(vq::FMT_NVFP4, epi, p, stream);
 }
 
+int32_t vq_gemm_nvfp4_noalloc(const uint16_t* x, const uint8_t* w, size_t w_bytes, float tensor_scale, void* y,
+                              int32_t y_dtype, int32_t M, int32_t N, int32_t K, int32_t epilogue, void* stream) {
+  if (!x || !w || !y) return fail(VQ_ERR_NULL, "vq_gemm_nvfp4_noalloc: x, w and y are required");
+  if (y_dtype != VQ_OUT_BF16 && y_dtype != VQ_OUT_F32) return fail(VQ_ERR_VALUE, "unknown y_dtype %d", y_dtype);
+  if (epilogue != VQ_EPI_NONE && epilogue != VQ_EPI_SILU_MUL) return fail(VQ_ERR_VALUE, "unknown epilogue %d", epilogue);
+  int32_t st = check_shape(M, N, K);
+  if (st) return st;
+  const bool silu = epilogue == VQ_EPI_SILU_MUL;
+  const int epi = silu ? vq::EPI_SILU : vq::EPI_NONE;
+  if (vq::tiles_for(epi, N) > vq::kScratchTiles)
+    return fail(VQ_ERR_SHAPE, "vq_gemm_nvfp4_noalloc: N = %d needs %d tiles, the device scratch holds %d (N <= %d%s)",
+                N, vq::tiles_for(epi, N), vq::kScratchTiles, silu ? vq::kScratchTiles * 32 : vq::kScratchTiles * 64,
+                silu ? " with SILU_MUL" : "");
+  if (!aligned(x, 16)) return fail(VQ_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(y, y_dtype == VQ_OUT_F32 ? 4 : 2)) return fail(VQ_ERR_ALIGN, "y is not aligned to its element size");
+  st = check_w(w, w_bytes, silu ? packed_bytes(VQ_PACK_NVFP4_GATE_UP, 2 * (int64_t)N, K)
+                                 : packed_bytes(VQ_PACK_NVFP4, N, K));
+  if (st) return st;
+  const vq::Schedule s = vq::make_schedule(epi, N, K);
+  if (s.wgs > vq::kCUs) return fail(VQ_ERR_SHAPE, "schedule of %d workgroups exceeds the scratch's %d", s.wgs, vq::kCUs);
+  st = check_device();
+  if (st) return st;
+  void* base = nullptr;
+  const int err = vq::scratch_ptr(&base);
+  if (err != 0)
+    return fail(VQ_ERR_DEVICE, "device scratch lookup failed: %s", hipGetErrorString((hipError_t)err));
+  char* sc = static_cast<char*>(base);
+  vq::GemmParams p{};
+  p.x = x;
+  p.w = w;
+  p.out_scale = tensor_scale;
+  p.y = y;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.y_f32 = y_dtype == VQ_OUT_F32;
+  p.zeros = reinterpret_cast<const uint16_t*>(sc);
+  p.counters = reinterpret_cast<uint32_t*>(sc + vq::kScratchCounters);
+  p.partials = reinterpret_cast<float*>(sc + vq::kScratchPartials);
+  p.tiles = s.tiles;
+  p.iters = s.iters;
+  p.total = s.total;
+  p.wgs = s.wgs;
+  return launch(vq::FMT_NVFP4, epi, p, stream);
+}
+
 int32_t vq_pack_affine_q4(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases, int32_t rows,
                           int32_t K, int32_t gate_up, uint8_t* packed, size_t packed_bytes_avail, void* stream) {
   if (!codes || !scales || !biases || !packed)

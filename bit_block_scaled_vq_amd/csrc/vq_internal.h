@@ -143,6 +143,20 @@ struct GdnParams {
   int32_t B, T, H, Hk, lanes;
 };
 
+// Device scratch of the allocation-free GEMM entry point: one fixed layout
+// for every shape, so calls of different (N, K, epilogue) can follow each
+// other on it: [256 B zero region][per-tile counters][partial-sum slots].
+// Counters start at zero (static storage) and every call leaves the ones it
+// used at zero; the slots need no initial value.
+constexpr int kScratchTiles = 1 << 16;                 // N <= 4,194,304 (2,097,152 with SILU_MUL)
+constexpr size_t kScratchZero = 256;
+constexpr size_t kScratchCounters = kScratchZero;
+constexpr size_t kScratchPartials = kScratchCounters + (size_t)kScratchTiles * sizeof(uint32_t);
+constexpr size_t kScratchBytes = kScratchPartials + (size_t)2 * kCUs * kSlotFloats * sizeof(float);
+// This device's copy of the scratch array (looked up once per device); 0 on
+// success, else the hipError_t of the lookup.
+int scratch_ptr(void** out);
+
 // Launchers: return 0 on success, else the hipError_t of the launch.
 int launch_gemm(int fmt, int epi, const GemmParams& p, void* stream);
 int launch_pack(int fmt, const PackParams& p, void* stream);

@@ -53,6 +53,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "vq_internal.h"
 #include "vq_keys.h"
 
@@ -963,6 +965,34 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4_t* __restri
   for (; i < n; i += st) acc ^= __builtin_nontemporal_load(src + i);
   // Never true for the probe's data in practice, but the compiler cannot know.
   if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u) sink[0] = acc;
+}
+
+// ------------------------------------------------------------------ scratch
+//
+// Device memory of the allocation-free GEMM entry point (the layout is in
+// vq_internal.h). In host code `scratch` names a host-side stand-in, never the
+// device address: hipGetSymbolAddress gives each device's own copy, and only
+// that pointer is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+}  // namespace
+
+int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return (int)hipErrorInvalidDevice;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return 0;
 }
 
 // ---------------------------------------------------------------- launchers

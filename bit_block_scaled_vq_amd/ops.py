@@ -42,7 +42,7 @@ VQ_PACK_AFFINE_Q4_GATE_UP = 4
 
 EXPORTS = [
     "vq_packed_bytes", "vq_pack_nvfp4", "vq_pack_fp8", "vq_pack_affine_q4", "vq_gemm_affine_q4",
-    "vq_gemm_nvfp4", "vq_gemm_fp8", "vq_lmhead_argmax_accept", "vq_sample_accept", "vq_gdn_verify",
+    "vq_gemm_nvfp4", "vq_gemm_nvfp4_noalloc", "vq_gemm_fp8", "vq_lmhead_argmax_accept", "vq_sample_accept", "vq_gdn_verify",
     "vq_gdn_commit", "vq_workspace_bytes",
     "vq_status_str", "vq_last_error", "vq_abi_version", "vq_probe_copy", "vq_probe_read",
 ]
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.vq_pack_fp8.restype = i32
     L.vq_gemm_nvfp4.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, i32, i32, vp, sz, vp]
     L.vq_gemm_nvfp4.restype = i32
+    L.vq_gemm_nvfp4_noalloc.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, i32, i32, vp]
+    L.vq_gemm_nvfp4_noalloc.restype = i32
     L.vq_pack_affine_q4.argtypes = [vp, vp, vp, i32, i32, i32, vp, sz, vp]
     L.vq_pack_affine_q4.restype = i32
     L.vq_gemm_affine_q4.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, vp, sz, vp]
@@ -258,6 +260,22 @@ def vq_gemm_nvfp4(x, w, tensor_scale: float, y, epilogue: int = VQ_EPI_NONE, wor
     ws_ptr, ws_n = _ws(workspace)
     _check(lib().vq_gemm_nvfp4(_ptr(x), _ptr(w), w.numel(), float(tensor_scale), _ptr(y),
                                _out_dtype(y), M, N, K, int(epilogue), ws_ptr, ws_n, _stream(stream)))
+    return y
+
+
+def vq_gemm_nvfp4_noalloc(x, w, tensor_scale: float, y, epilogue: int = VQ_EPI_NONE, stream=None):
+    """vq_gemm_nvfp4 with the library's static per-device scratch instead of a
+    workspace: nothing is allocated; calls that may overlap on one device race."""
+    torch = _torch()
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(w, "w", (torch.uint8,), 1)
+    _need(y, "y", (torch.bfloat16, torch.float32), 2)
+    M, K = x.shape
+    N = y.shape[1]
+    if y.shape[0] != M:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)} y {tuple(y.shape)}")
+    _check(lib().vq_gemm_nvfp4_noalloc(_ptr(x), _ptr(w), w.numel(), float(tensor_scale), _ptr(y),
+                                       _out_dtype(y), M, N, K, int(epilogue), _stream(stream)))
     return y
 
 

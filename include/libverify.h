@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define VQ_ABI_VERSION 5
+#define VQ_ABI_VERSION 6
 
 typedef enum {
   VQ_OK = 0,
@@ -150,6 +150,24 @@ int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* w, size_t w_bytes,
                       float tensor_scale, void* y, int32_t y_dtype,
                       int32_t M, int32_t N, int32_t K, int32_t epilogue,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* vq_gemm_nvfp4 without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Arguments, results and rounding are those
+ * of vq_gemm_nvfp4 (the same kernels and split-K schedule, so the outputs are
+ * bitwise equal); the partial sums and per-tile counters live in a static
+ * device array of the library, one per device, 256 B + 256 KiB + 8 MiB
+ * (8,651,008 bytes), allocated when the library's code is loaded on the device
+ * and held until the process ends. Limits: N <= 4,194,304 output columns
+ * (2,097,152 with VQ_EPI_SILU_MUL); larger N returns VQ_ERR_SHAPE. Every call
+ * on a device shares that device's array and leaves its counters at zero, so
+ * stream-ordered calls of any shape may follow each other, but calls that may
+ * overlap on one device (concurrent streams, graph branches) race on it and
+ * must use vq_gemm_nvfp4 with distinct workspaces instead. The call never
+ * allocates, frees or synchronises. */
+int32_t vq_gemm_nvfp4_noalloc(const uint16_t* x, const uint8_t* w, size_t w_bytes,
+                              float tensor_scale, void* y, int32_t y_dtype,
+                              int32_t M, int32_t N, int32_t K, int32_t epilogue, void* stream);
 
 /* Affine 4-bit weights ("144 tok/s needs 502 GB/s ...", section "The engine
  * hard-codes the model": per group of 64 inputs, 32 bytes of nibbles plus a

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = ops.lib()
-    assert L.vq_abi_version() == 5
+    assert L.vq_abi_version() == 6
     assert ops.status_str(ops.VQ_OK) == "VQ_OK"
     assert ops.status_str(ops.VQ_ERR_WORKSPACE) == "VQ_ERR_WORKSPACE"
     assert ops.status_str(99) == "VQ_ERR_UNKNOWN"
@@ -269,3 +269,25 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         ops.lib()
+
+
+def _noalloc(x=A, w=A, wn=1 << 30, y=A, yd=0, M=8, N=1024, K=512, epi=0):
+    return ops.lib().vq_gemm_nvfp4_noalloc(x, w, wn, 1.0, y, yd, M, N, K, epi, None)
+
+
+def test_gemm_nvfp4_noalloc_validation():
+    # the allocation-free variant checks the same arguments, plus the size its
+    # static scratch holds (65,536 tiles: N <= 4,194,304, or 2,097,152 with
+    # SILU_MUL), before any HIP call
+    assert _noalloc(x=None) == ops.VQ_ERR_NULL
+    assert _noalloc(w=None) == ops.VQ_ERR_NULL
+    assert _noalloc(M=0) == ops.VQ_ERR_SHAPE
+    assert _noalloc(M=33) == ops.VQ_ERR_SHAPE
+    assert _noalloc(K=96) == ops.VQ_ERR_SHAPE
+    assert _noalloc(yd=2) == ops.VQ_ERR_VALUE
+    assert _noalloc(epi=2) == ops.VQ_ERR_VALUE
+    assert _noalloc(N=4194305) == ops.VQ_ERR_SHAPE
+    assert "scratch" in ops.last_error()
+    assert _noalloc(N=2097153, epi=1) == ops.VQ_ERR_SHAPE
+    assert _noalloc(x=A + 8) == ops.VQ_ERR_ALIGN
+    assert _noalloc(wn=100) == ops.VQ_ERR_SHAPE
