@@ -26,6 +26,8 @@ FLAGS = [
     # result with VALU FMAs, and accumulation registers would add four
     # v_accvgpr_read per MFMA and serialise the MFMAs on one register quad
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # kernel arguments listed first are preloaded into SGPRs at wave launch
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

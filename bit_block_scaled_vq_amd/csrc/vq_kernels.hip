@@ -767,8 +767,24 @@ struct Occupancy {
 // touches it; if the tile also extends past [S, E), that sum is the
 // workgroup's piece of the tile and goes through the global stream-K fixup,
 // whose last-arriving workgroup sums the pieces in workgroup order.
+//
+// The values the prologue needs before the first weight load come first in
+// the argument list, so the dispatcher preloads them into SGPRs (kernel
+// arguments preloaded at wave launch, -amdgpu-kernarg-preload-count): the
+// first loads are issued without waiting on a kernel-argument fetch
+// (measured 1 % over the pass). The rest of the parameters follow in p.
 template <int FMT, int EPI, int RG>
-__global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kernel(
+    const uint8_t* a_w, const uint16_t* a_x, const uint16_t* a_zeros, int64_t a_total, int32_t a_wgs,
+    int32_t a_iters, int32_t a_K, int32_t a_M, GemmParams p) {
+  p.w = a_w;
+  p.x = a_x;
+  p.zeros = a_zeros;
+  p.total = a_total;
+  p.wgs = a_wgs;
+  p.iters = a_iters;
+  p.K = a_K;
+  p.M = a_M;
   using T = Traits<FMT, RG>;
   constexpr int PD = PipeDepth<FMT, RG>::value;
   constexpr int REGS = T::REGS;
@@ -1004,10 +1020,13 @@ static int launch_rg(const GemmParams& p, hipStream_t st) {
   const dim3 grid((unsigned)p.wgs), block(256);
   if constexpr (FMT == FMT_NVFP4) {
     (void)rg;  // launch_gemm sends M > 8 to the scaled family
-    hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
+                       p.iters, p.K, p.M, p);
   } else {
-    if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p);
+    if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
+                       p.iters, p.K, p.M, p);
+    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
+                       p.iters, p.K, p.M, p);
   }
   return (int)hipGetLastError();
 }
