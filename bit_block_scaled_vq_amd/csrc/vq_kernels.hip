@@ -747,7 +747,8 @@ __device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int l
 template <int FMT, int RG>
 struct PipeDepth {
   // wide row groups: the X ring would spill; scaled NVFP4 with two row groups
-  // trades ring depth for a second wave per SIMD (measured faster)
+  // keeps 2 (3 and 4 measured no faster at M = 24 and 32: there the second
+  // row group's activation loads and MFMAs set the pace, not the weight ring)
   static constexpr int value = (FMT == FMT_NVFP4S && RG == 2) ? 2 : (RG <= 2 ? 3 : 2);
 };
 // Workgroups per CU the register budget is sized for. Every launch has at
