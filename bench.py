@@ -70,8 +70,15 @@ def weight_bytes(fmt, n, k):
     return nvfp4_bytes(n, k)
 
 
-def act_bytes(n, k, m=M_ROWS):
-    return m * k * 2 + m * n * 2
+def act_bytes(n, k, m=M_ROWS, accumulate=False):
+    # accumulating launches write an fp32 output twice: the zero fill, then the sums
+    return m * k * 2 + (2 * m * n * 4 if accumulate else m * n * 2)
+
+
+# Launches that run the accumulating FP8 entry (fp32 output, zero on entry):
+# the narrow out-projections, whose split-K shares are added without an
+# exchange between workgroups.
+ACCUMULATE_KINDS = ("gdn_out", "attn_o")
 
 
 class Pass:
@@ -115,6 +122,12 @@ class Pass:
         self.h_final = inputs.device_x_bf16((5, 1002) + key, rows, HIDDEN, dev)
         self.y_in = torch.empty((rows, max(GDN_IN, ATTN_QGKV)), dtype=bf, device=dev)
         self.y_hid = torch.empty((rows, HIDDEN), dtype=bf, device=dev)
+        # one zeroed fp32 output per out-projection launch, cleared once per pass
+        self.acc_slot = {}
+        for i, it in enumerate(self.items):
+            if it[0] in ACCUMULATE_KINDS:
+                self.acc_slot[i] = len(self.acc_slot)
+        self.y_acc = torch.zeros((len(self.acc_slot), rows, HIDDEN), dtype=torch.float32, device=dev)
         self.h_mlp = torch.empty((rows, INTER), dtype=bf, device=dev)
         self.argmax = torch.empty((rows,), dtype=torch.int32, device=dev)
         self.maxlogit = torch.empty((rows,), dtype=torch.float32, device=dev)
@@ -122,13 +135,15 @@ class Pass:
         self.commit = torch.empty((self.lanes, M_ROWS), dtype=torch.int32, device=dev)
         self.drafts = torch.zeros((self.lanes, M_ROWS - 1), dtype=torch.int32, device=dev)
         self.weight_bytes = sum(weight_bytes(f, n, k) for _, f, n, k in self.items)
-        self.act_bytes = sum(act_bytes(n, k, rows) for _, _, n, k in self.items)
+        self.act_bytes = sum(act_bytes(n, k, rows, kind in ACCUMULATE_KINDS) for kind, _, n, k in self.items)
 
     def launch(self, i):
         ops = self.ops
         kind, fmt, n, k = self.items[i]
         w = self.w[i]
-        if fmt == "fp8":
+        if i in self.acc_slot:
+            ops.vq_gemm_fp8_accumulate(self.x_mix, w, 1.0, self.y_acc[self.acc_slot[i]])
+        elif fmt == "fp8":
             x = self.x_hidden if k == HIDDEN else self.x_mix
             y = self.y_hid
             if n != HIDDEN:
@@ -145,6 +160,7 @@ class Pass:
                                         workspace=self.ws[(ops.VQ_OP_LMHEAD, n, k)])
 
     def run(self):
+        self.y_acc.zero_()  # a fill kernel (graph-safe), part of the timed pass
         for i in range(len(self.items)):
             self.launch(i)
 
@@ -282,8 +298,12 @@ def m_sweep(torch, ops, inputs_mod, p, rows=(1, 8, 16, 24, 32), reps=2):
             op = {"fp8": ops.VQ_OP_FP8, "nvfp4": ops.VQ_OP_NVFP4, "nvfp4_silu": ops.VQ_OP_NVFP4_SILU_MUL}[fmt]
             ws = p.ws[(op, n, k)]
 
+            y32 = torch.zeros((m, n), dtype=torch.float32, device=dev)
+
             def run(i):
-                if fmt == "fp8":
+                if kind in ACCUMULATE_KINDS:
+                    ops.vq_gemm_fp8_accumulate(x, p.w[i], 1.0, y32)  # timing only: y32 is not cleared
+                elif fmt == "fp8":
                     ops.vq_gemm_fp8(x, p.w[i], 1.0, y, workspace=ws)
                 else:
                     ops.vq_gemm_nvfp4(x, p.w[i], 1.0, y, epilogue=ops.VQ_EPI_SILU_MUL if fmt == "nvfp4_silu"
@@ -506,6 +526,7 @@ def pass_with_state(torch, ops, inputs_mod, p, steps=10):
     per_layer = [tuple(x[l:l + 1] for x in (state, slot, q, k, v, a, b, o)) for l in range(L)]
 
     def run():
+        p.y_acc.zero_()
         layer = 0
         for i, item in enumerate(p.items):
             p.launch(i)
@@ -606,6 +627,7 @@ def sampled_verify(torch, ops, inputs_mod, p, g_steps=10, reps=20):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(st):
         with torch.cuda.graph(g, stream=st):
+            p.y_acc.zero_()
             for i in range(head):
                 p.launch(i)
             head_logits()

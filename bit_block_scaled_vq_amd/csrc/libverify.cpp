@@ -145,6 +145,14 @@ Schedule make_schedule(int epi, int32_t n_out, int32_t k) {
       break;
     }
   }
+  if (epi == EPI_ACC) {
+    // Every half-tile unit must be shared by at most two workgroups. Three
+    // workgroups per tile (stream-K over the tile's two units, boundaries at
+    // 2/3 and 4/3 of a unit) when that fits the CUs, else at most one
+    // workgroup per unit.
+    const int64_t pairs = s.tiles / 2;
+    g = 3 * pairs <= kCUs ? 3 * pairs : (s.tiles < kMaxWgs ? s.tiles : kMaxWgs);
+  }
   s.wgs = (int32_t)g;
   size_t off = 0;
   s.off_zero = off;
@@ -447,6 +455,34 @@ int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, size_t w_bytes, float w
   p.y_f32 = y_dtype == VQ_OUT_F32;
   bind_workspace(p, s, workspace);
   return launch(vq::FMT_FP8, vq::EPI_NONE, p, stream);
+}
+
+int32_t vq_gemm_fp8_accumulate(const uint16_t* x, const uint8_t* w, size_t w_bytes, float w_scale, float* y,
+                               int32_t M, int32_t N, int32_t K, void* stream) {
+  if (!x || !w || !y) return fail(VQ_ERR_NULL, "vq_gemm_fp8_accumulate: x, w and y are required");
+  int32_t st = check_shape(M, N, K);
+  if (st) return st;
+  if (!aligned(x, 16)) return fail(VQ_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(y, 4)) return fail(VQ_ERR_ALIGN, "y must be 4-byte aligned");
+  st = check_w(w, w_bytes, packed_bytes(VQ_PACK_FP8, N, K));
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  const vq::Schedule s = vq::make_schedule(vq::EPI_ACC, N, K);
+  vq::GemmParams p{};
+  p.x = x;
+  p.w = w;
+  p.out_scale = w_scale;
+  p.y = y;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.y_f32 = 1;
+  p.tiles = s.tiles;
+  p.iters = s.iters;
+  p.total = s.total;
+  p.wgs = s.wgs;  // no workspace: FP8 rows never read the zero region, and no shares are exchanged
+  return launch(vq::FMT_FP8, vq::EPI_ACC, p, stream);
 }
 
 int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* w, size_t w_bytes, float tensor_scale,

@@ -16,7 +16,7 @@ namespace vq {
 // and bias), 16 activation rows per row group; the packed block has the NVFP4
 // code layout and 512 B of (scale, bias) pairs.
 enum Fmt : int { FMT_NVFP4 = 0, FMT_FP8 = 1, FMT_NVFP4S = 2, FMT_AFFINE = 3 };
-enum Epi : int { EPI_NONE = 0, EPI_SILU = 1, EPI_ARGMAX = 2 };
+enum Epi : int { EPI_NONE = 0, EPI_SILU = 1, EPI_ARGMAX = 2, EPI_ACC = 3 };
 
 // Packed weights are laid out in blocks of one tile (64 weight rows, four
 // sub-tiles of 16) by one k-iteration (128 K). NVFP4 block: 4 KB of codes +
@@ -51,6 +51,8 @@ struct Schedule {
 // Tiles of an output of n_out columns: 64 columns per tile, or 32 with the
 // SiLU epilogue (whose tiles carry 32 gate + 32 up rows).
 inline int32_t tiles_for(int epi, int32_t n_out) {
+  // accumulating epilogue: both halves of every 64-row weight tile
+  if (epi == EPI_ACC) return 2 * ((n_out + kTileRows - 1) / kTileRows);
   const int32_t cols = epi == EPI_SILU ? kTileRows / 2 : kTileRows;
   return (n_out + cols - 1) / cols;
 }

@@ -50,6 +50,13 @@
 //    last-arriving workgroup in workgroup order (deterministic, independent of
 //    M). Cross-workgroup data moves only through agent-scope atomics, so no
 //    L2 write-back/invalidate is issued.
+//  * Accumulating FP8 epilogue (fp32 output, zero on entry): the units are
+//    half tiles (two sub-tiles, the first or second half of every block) and
+//    the schedule gives each unit at most two workgroup shares; every share
+//    is added into the output with one fp32 atomic add per element. From
+//    zero, 0 + a + b = 0 + b + a, so the result does not depend on the order
+//    in which the shares arrive, and no workgroup waits on another (no piece
+//    exchange, no counter, no final store after a round trip).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -318,28 +325,36 @@ struct Traits {
 template <int EPI>
 __device__ __forceinline__ int out_col(int tile, int t, int n) {
   if (EPI == EPI_SILU) return tile * (kTileRows / 2) + (t & 1) * kSub + n;
+  if (EPI == EPI_ACC) return tile * (kTileRows / 2) + t * kSub + n;  // tile = half-tile unit
   return tile * kTileRows + t * kSub + n;
 }
 
+// Sub-tiles per unit of the (unit, iteration) space: a whole 64-row tile, or
+// half of one (two sub-tiles) for the accumulating epilogue.
+template <int EPI>
+struct UnitSubs {
+  static constexpr int value = EPI == EPI_ACC ? kNT / 2 : kNT;
+};
+
 // ---------------------------------------------------------- per-iteration data
 
-template <int FMT>
+template <int FMT, int NT = kNT>
 struct WBuf;
 template <>
-struct WBuf<FMT_NVFP4> {
+struct WBuf<FMT_NVFP4, kNT> {
   u32x4_t c[kNT];  // per sub-tile: code dwords of MFMA steps 0..3
   u32x4_t s;       // per sub-tile: the 4 block scales of this lane's half
 };
 template <>
-struct WBuf<FMT_NVFP4S> : WBuf<FMT_NVFP4> {};
+struct WBuf<FMT_NVFP4S, kNT> : WBuf<FMT_NVFP4, kNT> {};
 template <>
-struct WBuf<FMT_AFFINE> {
+struct WBuf<FMT_AFFINE, kNT> {
   u32x4_t c[kNT];   // per sub-tile: code dwords of MFMA steps 0..3
   u32x4_t sb[2];    // (scale, bias) of this lane's row: sub-tiles 0,1 then 2,3; groups 0,1
 };
-template <>
-struct WBuf<FMT_FP8> {
-  u32x4_t c[kNT][2];  // per sub-tile: weights of MFMA steps (0,1) and (2,3)
+template <int NT>
+struct WBuf<FMT_FP8, NT> {
+  u32x4_t c[NT][2];  // per sub-tile: weights of MFMA steps (0,1) and (2,3)
 };
 template <int RG>
 struct XBuf {
@@ -353,8 +368,11 @@ __device__ __forceinline__ u32x4_t ldnt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
-template <int FMT>
-__device__ __forceinline__ void load_w(WBuf<FMT>& b, const uint8_t* blk, int lane) {
+// blk: the block, or for a half-tile unit (NT = 2, FP8 only) the start of the
+// half's two sub-tiles inside its block.
+template <int FMT, int NT>
+__device__ __forceinline__ void load_w(WBuf<FMT, NT>& b, const uint8_t* blk, int lane) {
+  static_assert(NT == kNT || FMT == FMT_FP8, "half-tile units are FP8 only");
   if constexpr (FMT == FMT_AFFINE) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) b.c[t] = ldnt(blk + t * 1024 + lane * 16);
@@ -366,7 +384,7 @@ __device__ __forceinline__ void load_w(WBuf<FMT>& b, const uint8_t* blk, int lan
     b.s = ldnt(blk + 4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
   } else {
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
+    for (int t = 0; t < NT; ++t) {
       b.c[t][0] = ldnt(blk + (t * 2 + 0) * 1024 + lane * 16);
       b.c[t][1] = ldnt(blk + (t * 2 + 1) * 1024 + lane * 16);
     }
@@ -403,12 +421,12 @@ struct XCursor {
   }
 };
 
-template <int FMT, int RG>
+template <int FMT, int RG, int NT = kNT>
 struct Acc {
-  float v[kNT][4 * RG];
+  float v[NT][4 * RG];
   __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int t = 0; t < kNT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 4 * RG; ++r) v[t][r] = 0.0f;
   }
@@ -417,30 +435,30 @@ struct Acc {
   __device__ __forceinline__ void combine() {
     if constexpr (FMT == FMT_NVFP4) {
 #pragma unroll
-      for (int t = 0; t < kNT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 4 * RG; ++r) v[t][r] = v[t][r] + __shfl_xor(v[t][r], 32);
     }
   }
 };
 
-template <int FMT, int RG>
-__device__ __forceinline__ void compute_iter(const WBuf<FMT>& b, const XBuf<RG>& x, Acc<FMT, RG>& acc) {
+template <int FMT, int RG, int NT>
+__device__ __forceinline__ void compute_iter(const WBuf<FMT, NT>& b, const XBuf<RG>& x, Acc<FMT, RG, NT>& acc) {
   if constexpr (FMT == FMT_NVFP4) {
     // All 16 MFMAs of the block first, each into its own result registers,
     // then the block-scale FMAs: the matrix unit's latency is covered by the
     // other MFMAs and the decodes instead of stalling every FMA chain (the
     // summation order per accumulator is unchanged: j = 0..3 within t).
     static_assert(RG == 1, "the block-scale-after-MFMA family serves M <= 8 (one row group)");
-    f32x4_t d[kNT][4];
+    f32x4_t d[NT][4];
 #pragma unroll
-    for (int t = 0; t < kNT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         d[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[0][j]),
                                                           dec_fp4x8(b.c[t][j]), f32x4_t{}, 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < kNT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float sc = scale_byte(b.s[t], j);
@@ -449,7 +467,7 @@ __device__ __forceinline__ void compute_iter(const WBuf<FMT>& b, const XBuf<RG>&
       }
   } else if constexpr (FMT == FMT_NVFP4S) {
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16x8_t wv = dec_fp4x8_scaled(b.c[t][j], scale_byte(b.s[t], j));
@@ -502,7 +520,7 @@ __device__ __forceinline__ void compute_iter(const WBuf<FMT>& b, const XBuf<RG>&
     }
   } else {
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4_t c = b.c[t][j >> 1];
@@ -583,7 +601,21 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int tile, int lane
     for (int r = 0; r < 4; ++r) {
       const int m = T::row(lane, rg, r);
       const int q = 4 * rg + r;
-      if constexpr (EPI == EPI_NONE) {
+      if constexpr (EPI == EPI_ACC) {
+        // a workgroup's share of a half-tile unit (the whole unit, or one of
+        // its two shares) is added into the fp32 output: from zero, 0 + a and
+        // 0 + a + b = 0 + b + a are exact in any order of arrival
+        if (m < p.M) {
+          float* y = static_cast<float*>(p.y);
+#pragma unroll
+          for (int t = 0; t < UnitSubs<EPI>::value; ++t) {
+            const int col = out_col<EPI>(tile, t, n);
+            if (col < p.N)
+              __hip_atomic_fetch_add(y + (size_t)m * p.N + col, get(t, q) * sc, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      } else if constexpr (EPI == EPI_NONE) {
         if (m < p.M) {
 #pragma unroll
           for (int t = 0; t < kNT; ++t) {
@@ -656,19 +688,19 @@ __device__ __forceinline__ bool holds_sum(int lane) {
 
 // A piece (one wave's or one workgroup's share of a tile) is stored as value
 // (t, r) of lane l at float index (t * REGS + r) * 64 + l.
-template <int FMT, int REGS>
-__device__ __forceinline__ void lds_put(float* slot, int lane, const float (&v)[kNT][REGS]) {
+template <int FMT, int REGS, int NT>
+__device__ __forceinline__ void lds_put(float* slot, int lane, const float (&v)[NT][REGS]) {
   if (!holds_sum<FMT>(lane)) return;
 #pragma unroll
-  for (int t = 0; t < kNT; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < REGS; ++r) slot[(t * REGS + r) * 64 + lane] = v[t][r];
 }
-template <int FMT, int REGS>
-__device__ __forceinline__ void lds_add(const float* slot, int lane, float (&v)[kNT][REGS]) {
+template <int FMT, int REGS, int NT>
+__device__ __forceinline__ void lds_add(const float* slot, int lane, float (&v)[NT][REGS]) {
   if (!holds_sum<FMT>(lane)) return;
 #pragma unroll
-  for (int t = 0; t < kNT; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < REGS; ++r) v[t][r] += slot[(t * REGS + r) * 64 + lane];
 }
@@ -744,12 +776,15 @@ __device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int l
 // Iterations in flight per wave. The vector-memory counter retires loads in
 // issue order, so X fragments share the weights' ring (a shallower X ring
 // would cap the weight prefetch at its depth).
-template <int FMT, int RG>
+template <int FMT, int RG, int NT = kNT>
 struct PipeDepth {
   // wide row groups: the X ring would spill; scaled NVFP4 with two row groups
   // keeps 2 (3 and 4 measured no faster at M = 24 and 32: there the second
-  // row group's activation loads and MFMAs set the pace, not the weight ring)
-  static constexpr int value = (FMT == FMT_NVFP4S && RG == 2) ? 2 : (RG <= 2 ? 3 : 2);
+  // row group's activation loads and MFMAs set the pace, not the weight ring).
+  // Half-tile units carry half the weight bytes per iteration: 5 deep at one
+  // row group (4 and 6 measured slower on 5,120 x 6,144 at M = 8).
+  static constexpr int value = NT < kNT ? (RG == 1 ? 5 : 3)
+                                        : (FMT == FMT_NVFP4S && RG == 2) ? 2 : (RG <= 2 ? 3 : 2);
 };
 // Workgroups per CU the register budget is sized for. Every launch has at
 // most one workgroup per CU (at most 256 workgroups of 4 waves), so one wave
@@ -787,9 +822,11 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
   p.K = a_K;
   p.M = a_M;
   using T = Traits<FMT, RG>;
-  constexpr int PD = PipeDepth<FMT, RG>::value;
+  constexpr int NT = UnitSubs<EPI>::value;
+  constexpr bool ACC = EPI == EPI_ACC;
+  constexpr int PD = PipeDepth<FMT, RG, NT>::value;
   constexpr int REGS = T::REGS;
-  constexpr int SLOT = kNT * REGS * 64;
+  constexpr int SLOT = NT * REGS * 64;
   constexpr size_t BLOCK = FMT == FMT_FP8 ? kBlockF8 : kBlockF4;
   __shared__ float lds[4 * SLOT];
 
@@ -809,26 +846,40 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
   bool lds_piece = false; // this wave's share of first_tile (entered mid-way) is in its LDS slot
   bool reg_piece = false; // acc holds this wave's share of ctile, which starts inside [s, e)
   int ctile = first_tile;
-  Acc<FMT, RG> acc;
+  Acc<FMT, RG, NT> acc;
   acc.zero();
 
   if (s < e) {
-    // The wave's weight stream is the contiguous run of blocks [s, e).
-    const uint8_t* wnext = p.w + (size_t)s * BLOCK;
+    // The wave's weight stream is the contiguous run of blocks [s, e); with
+    // half-tile units, unit u is half u & 1 of tile u >> 1 and its stream the
+    // first or second half of each of that tile's blocks.
+    constexpr size_t HALF = BLOCK / 2;  // FP8: sub-tiles 2 and 3 fill the second half of a block
+    auto unit_base = [&](int64_t u) { return p.w + (size_t)((u >> 1) * I) * BLOCK + (size_t)(u & 1) * HALF; };
+    int64_t lu = first_tile;  // unit of the next load
+    const uint8_t* wnext = ACC ? unit_base(lu) + (size_t)(s - lu * I) * BLOCK : p.w + (size_t)s * BLOCK;
     XCursor<FMT, RG> xc;
     xc.init(p, lane);
     int xkit = (int)(s - (int64_t)first_tile * I);
     int64_t lit = s;  // next iteration to load
 
-    WBuf<FMT> wb[PD];
+    WBuf<FMT, NT> wb[PD];
     XBuf<RG> xb[PD];
     auto load_next = [&](int qq) {
-      load_w<FMT>(wb[qq], wnext, lane);
+      load_w<FMT, NT>(wb[qq], wnext, lane);
       xc.load(xb[qq], xkit);
       if (lit + 1 < e) {  // loads past the range re-read the last iteration
         ++lit;
-        wnext += BLOCK;
-        if (++xkit == I) xkit = 0;
+        if constexpr (ACC) {
+          if (++xkit == I) {
+            xkit = 0;
+            wnext = unit_base(++lu);
+          } else {
+            wnext += BLOCK;
+          }
+        } else {
+          wnext += BLOCK;
+          if (++xkit == I) xkit = 0;
+        }
       }
     };
 #pragma unroll
@@ -843,7 +894,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
         epilogue<FMT, EPI, RG>(p, ctile, lane, [&](int t, int r) { return acc.get(t, r); }, best);
         ++finished;
       } else {
-        lds_put<FMT, REGS>(lds + q * SLOT, lane, acc.v);
+        lds_put<FMT, REGS, NT>(lds + q * SLOT, lane, acc.v);
         lds_piece = true;
       }
       acc.zero();
@@ -857,7 +908,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
     for (int64_t bl = 0; bl < blocks; ++bl) {
 #pragma unroll
       for (int qq = 0; qq < PD; ++qq) {
-        compute_iter<FMT, RG>(wb[qq], xb[qq], acc);
+        compute_iter<FMT, RG, NT>(wb[qq], xb[qq], acc);
         load_next(qq);
         if (++ckit == I) tile_end();
       }
@@ -866,14 +917,14 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
 #pragma unroll
     for (int qq = 0; qq < PD; ++qq) {
       if (qq < rem) {
-        compute_iter<FMT, RG>(wb[qq], xb[qq], acc);
+        compute_iter<FMT, RG, NT>(wb[qq], xb[qq], acc);
         if (++ckit == I) tile_end();
       }
     }
     if (ckit != 0) {  // the range ends inside ctile
       acc.combine();
       if (started_inside) {  // ... which is first_tile, entered mid-way
-        lds_put<FMT, REGS>(lds + q * SLOT, lane, acc.v);
+        lds_put<FMT, REGS, NT>(lds + q * SLOT, lane, acc.v);
         lds_piece = true;
       } else {
         reg_piece = true;
@@ -883,23 +934,25 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
   __syncthreads();
 
   // Adds the LDS shares of the later waves that start inside `tile`.
-  auto add_later_waves = [&](int tile, float (&sum)[kNT][REGS]) {
+  auto add_later_waves = [&](int tile, float (&sum)[NT][REGS]) {
     const int64_t tend = (int64_t)(tile + 1) * I;
     for (int q2 = q + 1; q2 < 4; ++q2) {
       const int64_t s2 = S + q2 * span / 4, e2 = S + (q2 + 1) * span / 4;
       if (s2 >= tend) break;
-      if (s2 < e2) lds_add<FMT, REGS>(lds + q2 * SLOT, lane, sum);
+      if (s2 < e2) lds_add<FMT, REGS, NT>(lds + q2 * SLOT, lane, sum);
     }
   };
   // Finishes `tile` from this workgroup's share: directly when the tile lies
-  // inside [S, E), else through the global fixup.
-  auto finish = [&](int tile, float (&sum)[kNT][REGS]) {
+  // inside [S, E), else through the global fixup; a half-tile unit's share is
+  // always added into the output.
+  auto finish = [&](int tile, float (&sum)[NT][REGS]) {
     const int64_t t0 = (int64_t)tile * I;
-    if (t0 >= S && t0 + I <= E) {
+    if (ACC || (t0 >= S && t0 + I <= E)) {  // accumulating: every share is added, no exchange
       epilogue<FMT, EPI, RG>(p, tile, lane, [&](int t, int r) { return sum[t][r]; }, best);
       ++finished;
       return;
     }
+    if constexpr (!ACC) {
     store_piece<FMT, REGS>(p, 2 * g + (tile == S / I ? 0 : 1), lane, sum);
     wait_stores();
     if (arrive(p, tile, lane)) {
@@ -908,6 +961,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
       epilogue<FMT, EPI, RG>(p, tile, lane, [&](int t, int r) { return tot[t][r]; }, best);
       ++finished;
     }
+    }
   };
 
   if (reg_piece) {  // this wave is the lowest one touching ctile
@@ -915,12 +969,12 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
     finish(ctile, acc.v);
   }
   if (lds_piece && s == S) {  // the workgroup starts inside first_tile: its first wave collects the share
-    float sum[kNT][REGS];
+    float sum[NT][REGS];
 #pragma unroll
-    for (int t = 0; t < kNT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < REGS; ++r) sum[t][r] = 0.0f;
-    lds_add<FMT, REGS>(lds + q * SLOT, lane, sum);
+    lds_add<FMT, REGS, NT>(lds + q * SLOT, lane, sum);
     add_later_waves(first_tile, sum);
     finish(first_tile, sum);
   }
@@ -1049,6 +1103,7 @@ int launch_gemm(int fmt, int epi, const GemmParams& p, void* stream) {
     if (epi == EPI_SILU) return launch_rg<FMT_AFFINE, EPI_SILU>(p, st);
     return launch_rg<FMT_AFFINE, EPI_NONE>(p, st);
   }
+  if (epi == EPI_ACC) return launch_rg<FMT_FP8, EPI_ACC>(p, st);
   return launch_rg<FMT_FP8, EPI_NONE>(p, st);
 }
 

@@ -42,8 +42,8 @@ VQ_PACK_AFFINE_Q4_GATE_UP = 4
 
 EXPORTS = [
     "vq_packed_bytes", "vq_pack_nvfp4", "vq_pack_fp8", "vq_pack_affine_q4", "vq_gemm_affine_q4",
-    "vq_gemm_nvfp4", "vq_gemm_nvfp4_noalloc", "vq_gemm_fp8", "vq_lmhead_argmax_accept", "vq_sample_accept", "vq_gdn_verify",
-    "vq_gdn_commit", "vq_workspace_bytes",
+    "vq_gemm_nvfp4", "vq_gemm_nvfp4_noalloc", "vq_gemm_fp8", "vq_gemm_fp8_accumulate", "vq_lmhead_argmax_accept",
+    "vq_sample_accept", "vq_gdn_verify", "vq_gdn_commit", "vq_workspace_bytes",
     "vq_status_str", "vq_last_error", "vq_abi_version", "vq_probe_copy", "vq_probe_read",
 ]
 
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.vq_gemm_affine_q4.restype = i32
     L.vq_gemm_fp8.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, i32, vp, sz, vp]
     L.vq_gemm_fp8.restype = i32
+    L.vq_gemm_fp8_accumulate.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, vp]
+    L.vq_gemm_fp8_accumulate.restype = i32
     L.vq_lmhead_argmax_accept.argtypes = [vp, vp, sz, f32, vp, i32, i32, i32, i32,
                                           vp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.vq_lmhead_argmax_accept.restype = i32
@@ -292,6 +294,22 @@ def vq_gemm_fp8(x, w, w_scale: float, y, workspace=None, stream=None):
     ws_ptr, ws_n = _ws(workspace)
     _check(lib().vq_gemm_fp8(_ptr(x), _ptr(w), w.numel(), float(w_scale), _ptr(y), _out_dtype(y), M, N, K,
                              ws_ptr, ws_n, _stream(stream)))
+    return y
+
+
+def vq_gemm_fp8_accumulate(x, w, w_scale: float, y, stream=None):
+    """y[M][N] (fp32) += (x . E4M3(W)^T) * w_scale, W packed by pack_fp8; no
+    workspace. Deterministic when y holds zeros on entry."""
+    torch = _torch()
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(w, "w", (torch.uint8,), 1)
+    _need(y, "y", (torch.float32,), 2)
+    M, K = x.shape
+    N = y.shape[1]
+    if y.shape[0] != M:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)} y {tuple(y.shape)}")
+    _check(lib().vq_gemm_fp8_accumulate(_ptr(x), _ptr(w), w.numel(), float(w_scale), _ptr(y), M, N, K,
+                                        _stream(stream)))
     return y
 
 

@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define VQ_ABI_VERSION 6
+#define VQ_ABI_VERSION 7
 
 typedef enum {
   VQ_OK = 0,
@@ -207,6 +207,24 @@ int32_t vq_gemm_affine_q4(const uint16_t* x, const uint8_t* w, size_t w_bytes, v
 int32_t vq_gemm_fp8(const uint16_t* x, const uint8_t* w, size_t w_bytes, float w_scale,
                     void* y, int32_t y_dtype, int32_t M, int32_t N, int32_t K,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* FP8 skinny GEMM added into an fp32 output: Y[M][N] += (X . E4M3(w)^T) *
+ * w_scale. Same operands and shapes as vq_gemm_fp8 (x bf16 [M][K], 16-byte
+ * aligned; w from vq_pack_fp8 of [N][K]); y fp32 [M][N], 4-byte aligned. No
+ * workspace. The split-K reduction is done by the additions themselves: the
+ * output columns are worked in units of 32, the schedule gives every unit
+ * at most two workgroup shares, and each share is added with one fp32
+ * atomic add per element, so no workgroup waits for another ("Beating
+ * Splash on an M5 Max ...", section "The kernels were not the gap": split-K
+ * on the narrow projections, here with a reduction whose result does not
+ * depend on arrival order). With y zero on entry the result is
+ * deterministic (0 + a + b = 0 + b + a: bitwise the same on every call);
+ * a nonzero y is added to, but the order of a unit's two shares is then not
+ * fixed. Meant for the narrow projections (N <= 5,440 fills the CUs with
+ * three workgroups per 64 columns); any N up to the vq_gemm_fp8 limits is
+ * accepted. */
+int32_t vq_gemm_fp8_accumulate(const uint16_t* x, const uint8_t* w, size_t w_bytes, float w_scale,
+                               float* y, int32_t M, int32_t N, int32_t K, void* stream);
 
 /* Vocabulary head + per-row argmax + greedy accept, all on the device
  * ("Beating Splash on an M5 Max ...", section "What actually moved the

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = ops.lib()
-    assert L.vq_abi_version() == 6
+    assert L.vq_abi_version() == 7
     assert ops.status_str(ops.VQ_OK) == "VQ_OK"
     assert ops.status_str(ops.VQ_ERR_WORKSPACE) == "VQ_ERR_WORKSPACE"
     assert ops.status_str(99) == "VQ_ERR_UNKNOWN"
@@ -79,6 +79,34 @@ def test_gemm_fp8_validation():
     assert L.vq_gemm_fp8(A, A + 2, big, 1.0, A, 0, 8, 64, 128, A, big, None) == ops.VQ_ERR_ALIGN
     assert L.vq_gemm_fp8(A, A, 8191, 1.0, A, 0, 8, 64, 128, A, big, None) == ops.VQ_ERR_SHAPE
     assert L.vq_gemm_fp8(A, A, big, 1.0, A, 0, 8, 64, 128, A, 0, None) == ops.VQ_ERR_WORKSPACE
+
+
+def test_gemm_fp8_accumulate_validation():
+    L = ops.lib()
+    big = 1 << 30
+    assert L.vq_gemm_fp8_accumulate(None, A, big, 1.0, A, 8, 64, 128, None) == ops.VQ_ERR_NULL
+    assert L.vq_gemm_fp8_accumulate(A, None, big, 1.0, A, 8, 64, 128, None) == ops.VQ_ERR_NULL
+    assert L.vq_gemm_fp8_accumulate(A, A, big, 1.0, None, 8, 64, 128, None) == ops.VQ_ERR_NULL
+    assert L.vq_gemm_fp8_accumulate(A, A, big, 1.0, A, 0, 64, 128, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_gemm_fp8_accumulate(A, A, big, 1.0, A, 33, 64, 128, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_gemm_fp8_accumulate(A, A, big, 1.0, A, 8, 0, 128, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_gemm_fp8_accumulate(A, A, big, 1.0, A, 8, 64, 100, None) == ops.VQ_ERR_SHAPE
+    assert L.vq_gemm_fp8_accumulate(A + 8, A, big, 1.0, A, 8, 64, 128, None) == ops.VQ_ERR_ALIGN
+    assert L.vq_gemm_fp8_accumulate(A, A + 2, big, 1.0, A, 8, 64, 128, None) == ops.VQ_ERR_ALIGN
+    assert L.vq_gemm_fp8_accumulate(A, A, big, 1.0, A + 2, 8, 64, 128, None) == ops.VQ_ERR_ALIGN
+    need = ops.packed_bytes(ops.VQ_PACK_FP8, 64, 128)
+    assert L.vq_gemm_fp8_accumulate(A, A, need - 1, 1.0, A, 8, 64, 128, None) == ops.VQ_ERR_SHAPE
+    assert "packed weights" in ops.last_error()
+
+
+def test_fp8_accumulate_binding_refuses_host_and_wrong_dtypes():
+    import torch
+    x = torch.zeros((8, 128), dtype=torch.bfloat16)
+    w = torch.zeros(8192, dtype=torch.uint8)
+    with pytest.raises(ValueError):  # host tensors are refused before any library call
+        ops.vq_gemm_fp8_accumulate(x, w, 1.0, torch.zeros((8, 64), dtype=torch.float32))
+    with pytest.raises(TypeError):  # the output must be fp32
+        ops.vq_gemm_fp8_accumulate(x.float(), w, 1.0, torch.zeros((8, 64), dtype=torch.bfloat16))
 
 
 def _head(h=A, draft=A, lanes=1, R=8, V=1000, K=256, am=A, al=A, logits=None, ld=1, ws=A, wsn=1 << 30):

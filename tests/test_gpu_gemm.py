@@ -369,3 +369,117 @@ def test_nvfp4_every_block_scale_code_bit_exact(m):
     # the decoded scales span the whole E4M3FN range, subnormals included
     used = O.E4M3FN_TABLE[scales]
     assert np.nanmax(used) == 448.0 and np.min(np.abs(used[used != 0])) == 2.0 ** -9
+
+
+# ------------------------------------------------- FP8 accumulating entry point
+
+def run_fp8_acc(x_bits, w, wscale, y0=None, reps=1):
+    """vq_gemm_fp8_accumulate into an fp32 output holding zeros (or y0)."""
+    torch, dev = torch_dev()
+    ops = _ops()
+    x = to_dev_bf16(x_bits)
+    wd = ops.pack_fp8(to_dev_u8(w))
+    m, n = x_bits.shape[0], w.shape[0]
+    outs = []
+    for _ in range(reps):
+        y = torch.zeros((m, n), dtype=torch.float32, device=dev)
+        if y0 is not None:
+            y.copy_(torch.from_numpy(y0))
+        ops.vq_gemm_fp8_accumulate(x, wd, wscale, y)
+        outs.append(y.cpu().numpy())
+    torch.cuda.synchronize()
+    return outs
+
+
+@pytest.mark.parametrize("m,n,k,ws", [
+    (1, 1, 128, 1.0), (8, 100, 512, 0.37), (13, 257, 640, 0.125), (32, 64, 1024, 1.0), (8, 5000, 6144, 1.0),
+    (24, 3000, 5120, 1.0), (8, 5120, 6144, 0.75), (32, 5120, 6144, 0.75), (8, 16384, 5120, 1.0),
+])
+def test_fp8_accumulate_matches_oracle_and_is_deterministic(m, n, k, ws):
+    # three workgroups per 64 columns up to N = 5,440 (each 32-column unit
+    # shared by two), one unit or more per workgroup beyond
+    say(f"case: FP8 accumulate M={m} N={n} K={k} scale={ws}")
+    x = inputs.x_bf16((112, m, n, k), m, k)
+    w = inputs.fp8_weights((112, m, n, k), n, k)
+    ref = O.gemm_fp8(x, w, ws)
+    outs = run_fp8_acc(x, w, ws, reps=3)
+    check_f32(outs[0], ref, what=f"fp8 accumulate M{m} N{n} K{k}")
+    # elementwise within the fp32-accumulation bound, like the standard entry
+    assert np.max(np.abs(outs[0] - ref)) <= 1e-5 * np.max(np.abs(ref))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0]), "two calls from zero differ"
+    std = run_fp8(x, w, ws, out="f32")["f32"]
+    assert np.max(np.abs(outs[0] - std)) <= 1e-5 * np.max(np.abs(ref))
+
+
+def test_fp8_accumulate_adds_into_y():
+    m, n, k = 8, 300, 768
+    x = inputs.x_bf16((113,), m, k)
+    w = inputs.fp8_weights((113,), n, k)
+    y0 = np.random.default_rng(113).standard_normal((m, n)).astype(np.float32)
+    ref = O.gemm_fp8(x, w, 0.5)
+    got = run_fp8_acc(x, w, 0.5, y0=y0)[0]
+    check_f32(got - y0.astype(np.float64), ref, what="accumulate onto y0")
+    assert np.max(np.abs(got - (y0 + ref))) <= 1e-5 * np.max(np.abs(y0 + ref))
+
+
+def test_fp8_accumulate_all_codes_one_hot():
+    # every E4M3 code through the accumulating path: the unit's other share
+    # adds an exact zero, so the output is the decoded code (+0 for -0: y
+    # starts at +0)
+    n, k = 256, 384
+    w = np.zeros((n, k), dtype=np.uint8)
+    w[:, 5] = np.arange(256, dtype=np.uint8)
+    x = np.zeros((1, k), dtype=np.uint16)
+    x[0, 5] = 0x3F80
+    got = run_fp8_acc(x, w, 1.0)[0][0].astype(np.float64)
+    ref = O.E4M3FN_TABLE
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def test_fp8_accumulate_rows_independent_of_m():
+    # the K partition and the two-share split depend only on (N, K), and
+    # 0 + a + b does not depend on the order: rows are bitwise the same for
+    # every M
+    torch, dev = torch_dev()
+    ops = _ops()
+    n, k = 5120, 6144
+    w = ops.pack_fp8(to_dev_u8(inputs.fp8_weights((114,), n, k)))
+    x32 = inputs.x_bf16((114,), 32, k)
+    outs = {}
+    for m in (32, 8, 1, 17):
+        say(f"case: FP8 accumulate out-projection M={m}")
+        y = torch.zeros((m, n), dtype=torch.float32, device=dev)
+        ops.vq_gemm_fp8_accumulate(to_dev_bf16(x32[:m]), w, 1.0, y)
+        outs[m] = y.cpu().numpy()
+    for m in (8, 1, 17):
+        assert np.array_equal(outs[m], outs[32][:m]), m
+
+
+def test_fp8_accumulate_graph_replay():
+    # captured with the zero fill (a kernel, not a memset node) in front of
+    # it; every replay, with eager work between them, equals the eager call
+    torch, dev = torch_dev()
+    ops = _ops()
+    m, n, k = 8, 5120, 6144
+    xd = to_dev_bf16(inputs.x_bf16((115,), m, k))
+    w = ops.pack_fp8(to_dev_u8(inputs.fp8_weights((115,), n, k)))
+    y = torch.zeros((m, n), dtype=torch.float32, device=dev)
+    ops.vq_gemm_fp8_accumulate(xd, w, 1.0, y)
+    eager = y.cpu().numpy()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            y.zero_()
+            ops.vq_gemm_fp8_accumulate(xd, w, 1.0, y)
+    torch.cuda.current_stream().wait_stream(st)
+    for rep in range(4):
+        y.fill_(float(rep + 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), eager), rep
+        ops.vq_gemm_fp8_accumulate(xd, w, 1.0, torch.zeros_like(y))  # eager work between replays

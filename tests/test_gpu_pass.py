@@ -17,7 +17,9 @@ is wired in"). The launches are chained through their outputs:
 The two steps that are not library calls stand in for the mixer core and for
 the residual + norm, which are outside this stream: a column slice and a
 power-of-two rescale (exact in bf16) that keeps magnitudes bounded without
-norms. Every launch of one (op, N, K) shares one workspace, as in bench.py.
+norms. The out-projections run as bench.py runs them: the accumulating FP8
+entry into a zeroed fp32 output (the fill is captured too), whose bf16 cast
+stands in for the residual + norm in front of the MLP. Every launch of one (op, N, K) shares one workspace, as in bench.py.
 The 17 library launches (plus the stand-ins) are captured once into a HIP
 graph with bf16 outputs and replayed; a second graph re-runs every launch on
 the first graph's bf16 inputs with fp32 outputs (the parity mode), and the
@@ -103,6 +105,7 @@ def test_pass_graph_layers_0_to_3_and_head_full_size():
     yi = [torch.empty((M, L["n_in"]), dtype=bf, device=dev) for L in layers]
     mix = [torch.empty((M, MIX_K), dtype=bf, device=dev) for _ in range(LAYERS)]
     yo = [torch.empty((M, HIDDEN), dtype=bf, device=dev) for _ in range(LAYERS)]
+    yo32 = [torch.empty((M, HIDDEN), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
     h = [torch.empty((M, INTER), dtype=bf, device=dev) for _ in range(LAYERS)]
     yd = [torch.empty((M, HIDDEN), dtype=bf, device=dev) for _ in range(LAYERS)]
     f_i = [torch.empty((M, L["n_in"]), dtype=torch.float32, device=dev) for L in layers]
@@ -122,7 +125,9 @@ def test_pass_graph_layers_0_to_3_and_head_full_size():
         for l, L in enumerate(layers):
             ops.vq_gemm_fp8(x[l], L["p_in"], 1.0, yi[l], workspace=wsp(ops.VQ_OP_FP8, L["n_in"], HIDDEN))
             mix[l].copy_(yi[l][:, :MIX_K])                      # stand-in for the mixer core
-            ops.vq_gemm_fp8(mix[l], L["p_out"], 1.0, yo[l], workspace=wsp(ops.VQ_OP_FP8, HIDDEN, MIX_K))
+            yo32[l].zero_()
+            ops.vq_gemm_fp8_accumulate(mix[l], L["p_out"], 1.0, yo32[l])
+            yo[l].copy_(yo32[l])                                # stand-in for the residual + norm
             ops.vq_gemm_nvfp4(yo[l], L["p_gu"], 1.0, h[l], epilogue=ops.VQ_EPI_SILU_MUL,
                               workspace=wsp(ops.VQ_OP_NVFP4_SILU_MUL, INTER, HIDDEN))
             ops.vq_gemm_nvfp4(h[l], L["p_dn"], 1.0, yd[l], workspace=wsp(ops.VQ_OP_NVFP4, HIDDEN, INTER))
@@ -134,7 +139,8 @@ def test_pass_graph_layers_0_to_3_and_head_full_size():
         """Every launch again on the bf16 graph's inputs, fp32 outputs."""
         for l, L in enumerate(layers):
             ops.vq_gemm_fp8(x[l], L["p_in"], 1.0, f_i[l], workspace=wsp(ops.VQ_OP_FP8, L["n_in"], HIDDEN))
-            ops.vq_gemm_fp8(mix[l], L["p_out"], 1.0, f_o[l], workspace=wsp(ops.VQ_OP_FP8, HIDDEN, MIX_K))
+            f_o[l].zero_()
+            ops.vq_gemm_fp8_accumulate(mix[l], L["p_out"], 1.0, f_o[l])
             ops.vq_gemm_nvfp4(yo[l], L["p_gu"], 1.0, f_h[l], epilogue=ops.VQ_EPI_SILU_MUL,
                               workspace=wsp(ops.VQ_OP_NVFP4_SILU_MUL, INTER, HIDDEN))
             ops.vq_gemm_nvfp4(h[l], L["p_dn"], 1.0, f_d[l], workspace=wsp(ops.VQ_OP_NVFP4, HIDDEN, INTER))
@@ -147,6 +153,8 @@ def test_pass_graph_layers_0_to_3_and_head_full_size():
         s = {f"{n}{l}": _bits(t[l]) for n, t in (("x", x), ("yi", yi), ("mix", mix), ("yo", yo), ("h", h), ("yd", yd))
              for l in range(LAYERS)}
         s["x4"] = _bits(x[LAYERS])
+        for l in range(LAYERS):
+            s[f"yo32{l}"] = yo32[l].cpu().numpy().copy()
         for n, t in (("am", am), ("al", al), ("cm", cm), ("mx", mx)):
             s[n] = t.cpu().numpy().copy()
         return s
@@ -184,8 +192,8 @@ def test_pass_graph_layers_0_to_3_and_head_full_size():
     scratch = torch.empty((M, HIDDEN), dtype=torch.float32, device=dev)
     for rep in range(3):
         say(f"  replay {rep}")
-        for t in yi + yo + h + yd + f_i + f_o + f_h + f_d + x[1:]:
-            t.zero_()
+        for t in yi + yo + yo32 + h + yd + f_i + f_o + f_h + f_d + x[1:]:
+            t.fill_(3.0)
         am.fill_(-7), al.fill_(-7), cm.fill_(-7)
         torch.cuda.synchronize()
         g16.replay()
@@ -228,6 +236,8 @@ def test_pass_graph_layers_0_to_3_and_head_full_size():
         assert np.array_equal(eager[f"mix{l}"], eager[f"yi{l}"][:, :MIX_K])
         check(f"layer {l} out-proj", eager[f"mix{l}"], f_o[l].cpu().numpy(), eager[f"yo{l}"],
               lambda xb, c: O.gemm_fp8(xb, L["w_out"].cpu().numpy(), 1.0), HIDDEN, full=True)
+        # the accumulating entry is deterministic: both graphs' outputs agree
+        assert np.array_equal(eager[f"yo32{l}"], f_o[l].cpu().numpy())
 
         def gu_ref(xb, c, L=L):
             rows = torch.from_numpy(np.concatenate([c, INTER + c])).to(dev)
