@@ -234,6 +234,24 @@ size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K) {
 
 size_t vq_packed_bytes(int32_t kind, int32_t rows, int32_t K) { return packed_bytes(kind, rows, K); }
 
+int32_t vq_schedule_info(int32_t op, int32_t N, int32_t K, int32_t* units, int32_t* iters, int32_t* workgroups) {
+  if (!units || !iters || !workgroups) return fail(VQ_ERR_NULL, "vq_schedule_info: outputs are required");
+  if (!shape_ok(8, N, K)) return fail(VQ_ERR_SHAPE, "vq_schedule_info: N = %d, K = %d out of range", N, K);
+  int epi;
+  switch (op) {
+    case VQ_OP_NVFP4: case VQ_OP_FP8: case VQ_OP_AFFINE_Q4: epi = vq::EPI_NONE; break;
+    case VQ_OP_NVFP4_SILU_MUL: case VQ_OP_AFFINE_Q4_SILU_MUL: epi = vq::EPI_SILU; break;
+    case VQ_OP_LMHEAD: epi = vq::EPI_ARGMAX; break;
+    case VQ_OP_FP8_ACCUMULATE: epi = vq::EPI_ACC; break;
+    default: return fail(VQ_ERR_VALUE, "vq_schedule_info: op %d has no GEMM schedule", op);
+  }
+  const vq::Schedule s = vq::make_schedule(epi, N, K);
+  *units = s.tiles;
+  *iters = s.iters;
+  *workgroups = s.wgs;
+  return VQ_OK;
+}
+
 int32_t vq_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, int32_t rows, int32_t K, int32_t gate_up,
                       uint8_t* packed, size_t packed_bytes_avail, void* stream) {
   if (!codes || !scales || !packed) return fail(VQ_ERR_NULL, "vq_pack_nvfp4: codes, scales and packed are required");

@@ -34,6 +34,7 @@ VQ_OP_LMHEAD = 3
 VQ_OP_SAMPLE = 4
 VQ_OP_AFFINE_Q4 = 5
 VQ_OP_AFFINE_Q4_SILU_MUL = 6
+VQ_OP_FP8_ACCUMULATE = 7
 VQ_PACK_NVFP4 = 0
 VQ_PACK_NVFP4_GATE_UP = 1
 VQ_PACK_FP8 = 2
@@ -43,7 +44,7 @@ VQ_PACK_AFFINE_Q4_GATE_UP = 4
 EXPORTS = [
     "vq_packed_bytes", "vq_pack_nvfp4", "vq_pack_fp8", "vq_pack_affine_q4", "vq_gemm_affine_q4",
     "vq_gemm_nvfp4", "vq_gemm_nvfp4_noalloc", "vq_gemm_fp8", "vq_gemm_fp8_accumulate", "vq_lmhead_argmax_accept",
-    "vq_sample_accept", "vq_gdn_verify", "vq_gdn_commit", "vq_workspace_bytes",
+    "vq_sample_accept", "vq_gdn_verify", "vq_gdn_commit", "vq_workspace_bytes", "vq_schedule_info",
     "vq_status_str", "vq_last_error", "vq_abi_version", "vq_probe_copy", "vq_probe_read",
 ]
 
@@ -95,6 +96,9 @@ def lib() -> ctypes.CDLL:
     L.vq_gdn_commit.restype = i32
     L.vq_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.vq_workspace_bytes.restype = sz
+    pi = ctypes.POINTER(i32)
+    L.vq_schedule_info.argtypes = [i32, i32, i32, pi, pi, pi]
+    L.vq_schedule_info.restype = i32
     L.vq_status_str.argtypes = [i32]
     L.vq_status_str.restype = ctypes.c_char_p
     L.vq_last_error.argtypes = []
@@ -158,6 +162,13 @@ def _out_dtype(t) -> int:
 
 def workspace_bytes(op: int, M: int, N: int, K: int) -> int:
     return int(lib().vq_workspace_bytes(op, M, N, K))
+
+
+def schedule_info(op: int, N: int, K: int):
+    """(units, iterations per unit, workgroups) of the split a call of op uses."""
+    u, i, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().vq_schedule_info(op, N, K, ctypes.byref(u), ctypes.byref(i), ctypes.byref(g)))
+    return u.value, i.value, g.value
 
 
 def workspace(op: int, M: int, N: int, K: int, device="cuda"):

@@ -107,7 +107,8 @@ typedef enum { VQ_OUT_BF16 = 0, VQ_OUT_F32 = 1 } vq_out_dtype;
 typedef enum { VQ_EPI_NONE = 0, VQ_EPI_SILU_MUL = 1 } vq_epilogue;
 typedef enum {
   VQ_OP_NVFP4 = 0, VQ_OP_NVFP4_SILU_MUL = 1, VQ_OP_FP8 = 2, VQ_OP_LMHEAD = 3, VQ_OP_SAMPLE = 4,
-  VQ_OP_AFFINE_Q4 = 5, VQ_OP_AFFINE_Q4_SILU_MUL = 6
+  VQ_OP_AFFINE_Q4 = 5, VQ_OP_AFFINE_Q4_SILU_MUL = 6,
+  VQ_OP_FP8_ACCUMULATE = 7 /* vq_gemm_fp8_accumulate: no workspace (schedule query only) */
 } vq_op;
 typedef enum {
   VQ_PACK_NVFP4 = 0, VQ_PACK_NVFP4_GATE_UP = 1, VQ_PACK_FP8 = 2,
@@ -371,6 +372,18 @@ int32_t vq_gdn_commit(const float* state_in, float* state_out, const float* q, c
  * with M, and the per-lane counters sit at an offset placed from (M, V), so a
  * sampling workspace is bound to one (M, V). */
 size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K);
+
+/* The split-K / stream-K schedule a call of `op` (not VQ_OP_SAMPLE) uses at
+ * (N, K), for inspection and host-side checks ("Beating Splash on an M5
+ * Max ...", section "The kernels were not the gap": split-K on the narrow
+ * projections). The iteration space is units x iterations, W = units * (K /
+ * 128); workgroup g of G owns iterations [g W / G, (g + 1) W / G), unit-major.
+ * A unit is a 64-row tile of the packed weights (64 output columns, 32 with
+ * SILU_MUL); for VQ_OP_FP8_ACCUMULATE half a tile (32 output columns), and
+ * then no unit is shared by more than two workgroups. Writes units,
+ * iterations per unit and G; returns VQ_OK, or VQ_ERR_NULL / VQ_ERR_SHAPE /
+ * VQ_ERR_VALUE. M does not enter: the schedule depends on (op, N, K) only. */
+int32_t vq_schedule_info(int32_t op, int32_t N, int32_t K, int32_t* units, int32_t* iters, int32_t* workgroups);
 
 const char* vq_status_str(int32_t status);
 const char* vq_last_error(void);
