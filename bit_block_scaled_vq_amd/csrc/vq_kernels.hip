@@ -391,14 +391,36 @@ __device__ __forceinline__ void load_w(WBuf<FMT, NT>& b, const uint8_t* blk, int
   }
 }
 
-// X cursor: per row group a row pointer (or the zero region with a k-stride
-// of 0 for the NVFP4 lanes that must hold zeros).
+// X cursor. Fragment mode (one row group, and the NVFP4 M <= 8 family): per
+// row group a row pointer (or the zero region with a k-stride of 0 for the
+// NVFP4 lanes that must hold zeros), each load one MFMA step's A operand: 16
+// rows x 64 B, half of 16 cache lines. Line mode (two or more 16-row groups of
+// the FP8, scaled NVFP4 and affine kernels): each load reads 8 rows x 128 B,
+// whole lines, half the line requests per byte; stage_x puts the fragments in
+// MFMA order through the wave's LDS area. Lane l reads row l >> 3 (+ 8 for the
+// second half of the group), 16-byte segment (l & 7) ^ (l >> 3) of the line,
+// which stage_x stores at position l & 7 of that row: the swizzle keeps its
+// fragment reads free of bank conflicts.
 template <int FMT, int RG>
 struct XCursor {
-  const uint16_t* row[RG];
+  static constexpr bool kLines = RG >= 2 && FMT != FMT_NVFP4;
+  const uint16_t* row[RG];   // fragment mode
+  const uint16_t* half[RG];  // line mode: rows 0-7 in row[], rows 8-15 here
   int kstep;
   int jstep;
   __device__ __forceinline__ void init(const GemmParams& p, int lane) {
+    if constexpr (kLines) {
+      const int r = lane >> 3, seg = (lane & 7) ^ r;
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        int m0 = 16 * rg + r, m1 = m0 + 8;
+        m0 = m0 < p.M ? m0 : p.M - 1;  // rows past M are padding: any valid row will do
+        m1 = m1 < p.M ? m1 : p.M - 1;
+        row[rg] = p.x + (size_t)m0 * p.K + 8 * seg;
+        half[rg] = p.x + (size_t)m1 * p.K + 8 * seg;
+      }
+      return;
+    }
     const int i = lane & 15, g = lane >> 4;
     bool carries = true;
     if (FMT == FMT_NVFP4) carries = (i >> 3) == (g >> 1);
@@ -411,7 +433,21 @@ struct XCursor {
     kstep = carries ? kIterK : 0;
     jstep = carries ? 32 : 0;
   }
+  // Fragment mode: b.xa[rg][j] is MFMA step j's A operand. Line mode:
+  // b.xa[rg][c] holds rows 8 (c & 1) .. +7 of k 64 (c >> 1) .. +63.
   __device__ __forceinline__ void load(XBuf<RG>& b, int kit) const {
+    if constexpr (kLines) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        const uint16_t* lo = row[rg] + (size_t)(kit * kIterK);
+        const uint16_t* hi = half[rg] + (size_t)(kit * kIterK);
+        b.xa[rg][0] = ld16(lo);
+        b.xa[rg][1] = ld16(hi);
+        b.xa[rg][2] = ld16(lo + 64);
+        b.xa[rg][3] = ld16(hi + 64);
+      }
+      return;
+    }
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
       const uint16_t* xr = row[rg] + (size_t)(kit * kstep);
@@ -420,6 +456,35 @@ struct XCursor {
     }
   }
 };
+
+// Line-mode staging: one chunk per (row group, load) holds 8 rows x 128 B;
+// 1152 B per chunk rather than 1024 puts the two row halves of a fragment
+// read on different banks.
+constexpr int kXChunk = 72;  // u32x4 per chunk
+
+// Line-mode registers (see XCursor::load) -> MFMA A operands, through this
+// wave's LDS area xs (RG * 4 chunks). The wave barriers keep the compiler from
+// moving the LDS reads above the writes, or the next call's writes above this
+// call's reads; a wave's LDS operations execute in order.
+template <int RG>
+__device__ __forceinline__ void stage_x(const XBuf<RG>& in, XBuf<RG>& out, u32x4_t* xs, int lane) {
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xs[(rg * 4 + c) * kXChunk + lane] = in.xa[rg][c];
+  __builtin_amdgcn_wave_barrier();
+  const int i = lane & 15, g = lane >> 4;  // MFMA A operand: row i, k 8 g .. +7 of the step
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 2 * (j >> 1) + (i >> 3);
+      const int seg = 4 * (j & 1) + g;
+      out.xa[rg][j] = xs[(rg * 4 + c) * kXChunk + (i & 7) * 8 + (seg ^ (i & 7))];
+    }
+  __builtin_amdgcn_wave_barrier();
+}
 
 template <int FMT, int RG, int NT = kNT>
 struct Acc {
@@ -779,8 +844,8 @@ __device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int l
 template <int FMT, int RG, int NT = kNT>
 struct PipeDepth {
   // wide row groups: the X ring would spill; scaled NVFP4 with two row groups
-  // keeps 2 (3 and 4 measured no faster at M = 24 and 32: there the second
-  // row group's activation loads and MFMAs set the pace, not the weight ring).
+  // keeps 2 (3 and 4 measured slower at M = 24 and 32, with fragment-mode and
+  // with line-mode activation loads).
   // Half-tile units carry half the weight bytes per iteration: 5 deep at one
   // row group (4 and 6 measured slower on 5,120 x 6,144 at M = 8).
   static constexpr int value = NT < kNT ? (RG == 1 ? 5 : 3)
@@ -829,6 +894,9 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
   constexpr int SLOT = NT * REGS * 64;
   constexpr size_t BLOCK = FMT == FMT_FP8 ? kBlockF8 : kBlockF4;
   __shared__ float lds[4 * SLOT];
+  constexpr bool LINES = XCursor<FMT, RG>::kLines;
+  constexpr int XS = RG * 4 * kXChunk;  // line-mode staging per wave
+  __shared__ u32x4_t xstage[LINES ? 4 * XS : 1];
 
   const int lane = threadIdx.x & 63;
   const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -888,6 +956,16 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
     int ckit = (int)(s - (int64_t)first_tile * I);
     bool started_inside = ckit != 0;
 
+    auto compute = [&](int qq) {
+      if constexpr (LINES) {
+        XBuf<RG> xt;
+        stage_x<RG>(xb[qq], xt, xstage + q * XS, lane);
+        compute_iter<FMT, RG, NT>(wb[qq], xt, acc);
+      } else {
+        compute_iter<FMT, RG, NT>(wb[qq], xb[qq], acc);
+      }
+    };
+
     auto tile_end = [&]() {
       acc.combine();
       if (!started_inside) {
@@ -908,7 +986,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
     for (int64_t bl = 0; bl < blocks; ++bl) {
 #pragma unroll
       for (int qq = 0; qq < PD; ++qq) {
-        compute_iter<FMT, RG, NT>(wb[qq], xb[qq], acc);
+        compute(qq);
         load_next(qq);
         if (++ckit == I) tile_end();
       }
@@ -917,7 +995,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
 #pragma unroll
     for (int qq = 0; qq < PD; ++qq) {
       if (qq < rem) {
-        compute_iter<FMT, RG, NT>(wb[qq], xb[qq], acc);
+        compute(qq);
         if (++ckit == I) tile_end();
       }
     }

@@ -101,6 +101,7 @@ def test_nvfp4_single_gemm_m8_k512_n1024():
     (1, 1, 128, 1.0), (3, 33, 384, 0.37), (8, 100, 512, 1.0), (13, 257, 640, 2.5),
     (24, 64, 1024, 1.0), (32, 200, 256, 0.125), (8, 4096, 2048, 1.0), (5, 1000, 5120, 1.0),
     (16, 2, 128, 1.0), (8, 65, 128, 1.0), (9, 130, 768, 1.0), (7, 3000, 17408, 1.0),
+    (17, 70, 384, 1.0), (29, 130, 640, 0.5),
 ])
 def test_nvfp4_shapes(m, n, k, ts):
     say(f"case: NVFP4 M={m} N={n} K={k} ts={ts}")
@@ -180,7 +181,7 @@ def test_mlp_layer_m8_full_size():
 
 @pytest.mark.parametrize("m,n,k,ws", [
     (1, 1, 128, 1.0), (8, 100, 512, 0.37), (13, 257, 640, 0.125), (32, 64, 1024, 1.0), (8, 1000, 6144, 1.0),
-    (24, 3000, 5120, 1.0),
+    (24, 3000, 5120, 1.0), (17, 70, 384, 1.0), (29, 130, 640, 0.5),
 ])
 def test_fp8_shapes(m, n, k, ws):
     say(f"case: FP8 M={m} N={n} K={k} scale={ws}")
@@ -204,6 +205,31 @@ def test_fp8_all_codes_one_hot():
     got = r["f32"][0].astype(np.float64)
     same = (got == ref) | (np.isnan(got) & np.isnan(ref))
     assert same.all()
+
+
+@pytest.mark.parametrize("m", [32, 24, 17])
+def test_wide_rows_one_hot_row_map(m):
+    # Row r of X is one-hot at k_r (k_r spread over both 128-B lines of an
+    # iteration, every 16-B segment and both row halves of a 16-row group), so
+    # Y[r] must be exactly column k_r of the decoded weights: pins which
+    # activation row and k reach each MFMA lane when two or more row groups
+    # read whole lines and reorder them in LDS.
+    n, k = 96, 256
+    ks = [(37 * r + 5) % k for r in range(m)]
+    x = np.zeros((m, k), dtype=np.uint16)
+    for r, kk in enumerate(ks):
+        x[r, kk] = 0x3F80
+    say(f"case: one-hot rows NVFP4 M={m}")
+    codes, scales = inputs.nvfp4_weights((115, m), n, k)
+    wdq = O.dequant_nvfp4(codes, scales, 1.0).astype(np.float32)
+    got = run_nvfp4(x, codes, scales, 1.0, n, out="f32")["f32"]
+    for r, kk in enumerate(ks):
+        assert np.array_equal(got[r], wdq[:, kk]), (r, kk)
+    say(f"case: one-hot rows FP8 M={m}")
+    w8 = inputs.fp8_weights((115, m), n, k)
+    got = run_fp8(x, w8, 1.0, out="f32")["f32"]
+    for r, kk in enumerate(ks):
+        assert np.array_equal(got[r].astype(np.float64), O.E4M3FN_TABLE[w8[:, kk]]), (r, kk)
 
 
 # ---------------------------------------------- properties of the schedule
