@@ -391,19 +391,20 @@ __device__ __forceinline__ void load_w(WBuf<FMT, NT>& b, const uint8_t* blk, int
   }
 }
 
-// X cursor. Fragment mode (one row group, and the NVFP4 M <= 8 family): per
-// row group a row pointer (or the zero region with a k-stride of 0 for the
-// NVFP4 lanes that must hold zeros), each load one MFMA step's A operand: 16
-// rows x 64 B, half of 16 cache lines. Line mode (two or more 16-row groups of
-// the FP8, scaled NVFP4 and affine kernels): each load reads 8 rows x 128 B,
-// whole lines, half the line requests per byte; stage_x puts the fragments in
+// X cursor. Fragment mode (FP8 and affine at one row group, and the NVFP4
+// M <= 8 family): per row group a row pointer (or the zero region with a
+// k-stride of 0 for the NVFP4 lanes that must hold zeros), each load one MFMA
+// step's A operand: 16 rows x 64 B, half of 16 cache lines. Line mode (the
+// scaled NVFP4 family, and FP8 and affine at two or more 16-row groups): each
+// load reads 8 rows x 128 B, whole lines, half the line requests per byte;
+// stage_x puts the fragments in
 // MFMA order through the wave's LDS area. Lane l reads row l >> 3 (+ 8 for the
 // second half of the group), 16-byte segment (l & 7) ^ (l >> 3) of the line,
 // which stage_x stores at position l & 7 of that row: the swizzle keeps its
 // fragment reads free of bank conflicts.
 template <int FMT, int RG>
 struct XCursor {
-  static constexpr bool kLines = RG >= 2 && FMT != FMT_NVFP4;
+  static constexpr bool kLines = (RG >= 2 && FMT != FMT_NVFP4) || FMT == FMT_NVFP4S;
   const uint16_t* row[RG];   // fragment mode
   const uint16_t* half[RG];  // line mode: rows 0-7 in row[], rows 8-15 here
   int kstep;
