@@ -391,26 +391,32 @@ __device__ __forceinline__ void load_w(WBuf<FMT, NT>& b, const uint8_t* blk, int
   }
 }
 
-// X cursor. Fragment mode (FP8 and affine at one row group, and the NVFP4
-// M <= 8 family): per row group a row pointer (or the zero region with a
-// k-stride of 0 for the NVFP4 lanes that must hold zeros), each load one MFMA
-// step's A operand: 16 rows x 64 B, half of 16 cache lines. Line mode (the
-// scaled NVFP4 family, and FP8 and affine at two or more 16-row groups): each
-// load reads 8 rows x 128 B, whole lines, half the line requests per byte;
-// stage_x puts the fragments in
-// MFMA order through the wave's LDS area. Lane l reads row l >> 3 (+ 8 for the
-// second half of the group), 16-byte segment (l & 7) ^ (l >> 3) of the line,
-// which stage_x stores at position l & 7 of that row: the swizzle keeps its
+// X cursor: how each iteration's activation rows reach the MFMA A operands.
+//  kFrag (FP8 and affine at one row group): each load is one MFMA step's A
+//    operand, 16 rows x 64 B, half of 16 cache lines.
+//  kLines16 (the scaled NVFP4 family, and FP8 and affine at two or more
+//    16-row groups): each load reads 8 rows x 128 B, whole lines, half the
+//    line requests per byte; 4 loads per row group.
+//  kLines8 (the NVFP4 M <= 8 family): 2 loads per iteration, the 8 rows x
+//    128 B of each half of the iteration's k range. Its A operand holds the
+//    rows twice with zeros in between (rows 0-7 on k-groups 0,1, rows 8-15 on
+//    k-groups 2,3; see compute_iter); the zero lanes read a zeroed slot.
+// In the line modes lane l reads row l >> 3 (+ 8 for the second half of a
+// 16-row group), 16-byte segment (l & 7) ^ (l >> 3) of the line, and stage_x
+// puts the fragments in MFMA order through the wave's LDS area, where the
+// lane's 16 bytes land at position l & 7 of that row: the swizzle keeps the
 // fragment reads free of bank conflicts.
+enum XMode { kFrag = 0, kLines16 = 1, kLines8 = 2 };
+
 template <int FMT, int RG>
 struct XCursor {
-  static constexpr bool kLines = (RG >= 2 && FMT != FMT_NVFP4) || FMT == FMT_NVFP4S;
-  const uint16_t* row[RG];   // fragment mode
-  const uint16_t* half[RG];  // line mode: rows 0-7 in row[], rows 8-15 here
-  int kstep;
-  int jstep;
+  static constexpr int kMode =
+      FMT == FMT_NVFP4 ? kLines8 : ((RG >= 2 || FMT == FMT_NVFP4S) ? kLines16 : kFrag);
+  static_assert(kMode != kLines8 || RG == 1, "the NVFP4 M <= 8 family has one row group");
+  const uint16_t* row[RG];   // fragment mode: the lane's row; line modes: rows 0-7
+  const uint16_t* half[RG];  // kLines16: rows 8-15
   __device__ __forceinline__ void init(const GemmParams& p, int lane) {
-    if constexpr (kLines) {
+    if constexpr (kMode != kFrag) {
       const int r = lane >> 3, seg = (lane & 7) ^ r;
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
@@ -423,21 +429,22 @@ struct XCursor {
       return;
     }
     const int i = lane & 15, g = lane >> 4;
-    bool carries = true;
-    if (FMT == FMT_NVFP4) carries = (i >> 3) == (g >> 1);
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      int m = FMT == FMT_NVFP4 ? 8 * rg + (i & 7) : 16 * rg + i;
-      m = m < p.M ? m : p.M - 1;  // rows past M are padding: any valid row will do
-      row[rg] = carries ? p.x + (size_t)m * p.K + 8 * g : p.zeros;
+      int m = 16 * rg + i;
+      m = m < p.M ? m : p.M - 1;
+      row[rg] = p.x + (size_t)m * p.K + 8 * g;
     }
-    kstep = carries ? kIterK : 0;
-    jstep = carries ? 32 : 0;
   }
-  // Fragment mode: b.xa[rg][j] is MFMA step j's A operand. Line mode:
-  // b.xa[rg][c] holds rows 8 (c & 1) .. +7 of k 64 (c >> 1) .. +63.
+  // kFrag: b.xa[rg][j] is MFMA step j's A operand. kLines16: b.xa[rg][c]
+  // holds rows 8 (c & 1) .. +7 of k 64 (c >> 1) .. +63. kLines8: b.xa[0][c],
+  // c = 0, 1, holds rows 0-7 of k 64 c .. +63.
   __device__ __forceinline__ void load(XBuf<RG>& b, int kit) const {
-    if constexpr (kLines) {
+    if constexpr (kMode == kLines8) {
+      const uint16_t* lo = row[0] + (size_t)(kit * kIterK);
+      b.xa[0][0] = ld16(lo);
+      b.xa[0][1] = ld16(lo + 64);
+    } else if constexpr (kMode == kLines16) {
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
         const uint16_t* lo = row[rg] + (size_t)(kit * kIterK);
@@ -447,43 +454,60 @@ struct XCursor {
         b.xa[rg][2] = ld16(lo + 64);
         b.xa[rg][3] = ld16(hi + 64);
       }
-      return;
-    }
+    } else {
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-      const uint16_t* xr = row[rg] + (size_t)(kit * kstep);
+      for (int rg = 0; rg < RG; ++rg) {
+        const uint16_t* xr = row[rg] + (size_t)(kit * kIterK);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b.xa[rg][j] = ld16(xr + j * jstep);
+        for (int j = 0; j < 4; ++j) b.xa[rg][j] = ld16(xr + j * 32);
+      }
     }
   }
 };
 
 // Line-mode staging: one chunk per (row group, load) holds 8 rows x 128 B;
 // 1152 B per chunk rather than 1024 puts the two row halves of a fragment
-// read on different banks.
+// read on different banks. kLines8 adds one zeroed 16-byte slot after its two
+// chunks.
 constexpr int kXChunk = 72;  // u32x4 per chunk
+template <int MODE, int RG>
+struct XStage {
+  static constexpr int kZero = 2 * kXChunk;  // kLines8: the zero slot
+  static constexpr int kSize = MODE == kLines8 ? 2 * kXChunk + 8 : MODE == kLines16 ? 4 * RG * kXChunk : 0;
+};
 
 // Line-mode registers (see XCursor::load) -> MFMA A operands, through this
-// wave's LDS area xs (RG * 4 chunks). The wave barriers keep the compiler from
-// moving the LDS reads above the writes, or the next call's writes above this
-// call's reads; a wave's LDS operations execute in order.
-template <int RG>
+// wave's LDS area xs. The wave barriers keep the compiler from moving the LDS
+// reads above the writes, or the next call's writes above this call's reads;
+// a wave's LDS operations execute in order.
+template <int MODE, int RG>
 __device__ __forceinline__ void stage_x(const XBuf<RG>& in, XBuf<RG>& out, u32x4_t* xs, int lane) {
   __builtin_amdgcn_wave_barrier();
+  constexpr int NC = MODE == kLines8 ? 2 : 4;
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) xs[(rg * 4 + c) * kXChunk + lane] = in.xa[rg][c];
+    for (int c = 0; c < NC; ++c) xs[(rg * NC + c) * kXChunk + lane] = in.xa[rg][c];
   __builtin_amdgcn_wave_barrier();
   const int i = lane & 15, g = lane >> 4;  // MFMA A operand: row i, k 8 g .. +7 of the step
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
+  if constexpr (MODE == kLines8) {
+    const bool carries = (i >> 3) == (g >> 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = 2 * (j >> 1) + (i >> 3);
       const int seg = 4 * (j & 1) + g;
-      out.xa[rg][j] = xs[(rg * 4 + c) * kXChunk + (i & 7) * 8 + (seg ^ (i & 7))];
+      const int at = carries ? (j >> 1) * kXChunk + (i & 7) * 8 + (seg ^ (i & 7)) : XStage<MODE, RG>::kZero;
+      out.xa[0][j] = xs[at];
     }
+  } else {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 2 * (j >> 1) + (i >> 3);
+        const int seg = 4 * (j & 1) + g;
+        out.xa[rg][j] = xs[(rg * 4 + c) * kXChunk + (i & 7) * 8 + (seg ^ (i & 7))];
+      }
+  }
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -895,8 +919,9 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
   constexpr int SLOT = NT * REGS * 64;
   constexpr size_t BLOCK = FMT == FMT_FP8 ? kBlockF8 : kBlockF4;
   __shared__ float lds[4 * SLOT];
-  constexpr bool LINES = XCursor<FMT, RG>::kLines;
-  constexpr int XS = RG * 4 * kXChunk;  // line-mode staging per wave
+  constexpr int XMODE = XCursor<FMT, RG>::kMode;
+  constexpr bool LINES = XMODE != kFrag;
+  constexpr int XS = XStage<XMODE, RG>::kSize;  // line-mode staging per wave
   __shared__ u32x4_t xstage[LINES ? 4 * XS : 1];
 
   const int lane = threadIdx.x & 63;
@@ -928,6 +953,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
     const uint8_t* wnext = ACC ? unit_base(lu) + (size_t)(s - lu * I) * BLOCK : p.w + (size_t)s * BLOCK;
     XCursor<FMT, RG> xc;
     xc.init(p, lane);
+    if constexpr (XMODE == kLines8) xstage[q * XS + XStage<XMODE, RG>::kZero] = u32x4_t{0u, 0u, 0u, 0u};
     int xkit = (int)(s - (int64_t)first_tile * I);
     int64_t lit = s;  // next iteration to load
 
@@ -960,7 +986,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
     auto compute = [&](int qq) {
       if constexpr (LINES) {
         XBuf<RG> xt;
-        stage_x<RG>(xb[qq], xt, xstage + q * XS, lane);
+        stage_x<XMODE, RG>(xb[qq], xt, xstage + q * XS, lane);
         compute_iter<FMT, RG, NT>(wb[qq], xt, acc);
       } else {
         compute_iter<FMT, RG, NT>(wb[qq], xb[qq], acc);
