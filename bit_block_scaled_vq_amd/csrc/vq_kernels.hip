@@ -397,10 +397,12 @@ __device__ __forceinline__ void load_w(WBuf<FMT, NT>& b, const uint8_t* blk, int
 //  kLines16 (the scaled NVFP4 family, and FP8 and affine at two or more
 //    16-row groups): each load reads 8 rows x 128 B, whole lines, half the
 //    line requests per byte; 4 loads per row group.
-//  kLines8 (the NVFP4 M <= 8 family): 2 loads per iteration, the 8 rows x
-//    128 B of each half of the iteration's k range. Its A operand holds the
-//    rows twice with zeros in between (rows 0-7 on k-groups 0,1, rows 8-15 on
-//    k-groups 2,3; see compute_iter); the zero lanes read a zeroed slot.
+//  kLines8 (M <= 8: the NVFP4 M <= 8 family, and the FP8 and affine kernels
+//    instantiated for at most 8 rows): 2 loads per iteration, the 8 rows x
+//    128 B of each half of the iteration's k range. The NVFP4 A operand holds
+//    the rows twice with zeros in between (rows 0-7 on k-groups 0,1, rows
+//    8-15 on k-groups 2,3; see compute_iter); the 16-row kernels' rows 8-15
+//    are padding. Lanes that hold zeros read a zeroed slot.
 // In the line modes lane l reads row l >> 3 (+ 8 for the second half of a
 // 16-row group), 16-byte segment (l & 7) ^ (l >> 3) of the line, and stage_x
 // puts the fragments in MFMA order through the wave's LDS area, where the
@@ -408,10 +410,10 @@ __device__ __forceinline__ void load_w(WBuf<FMT, NT>& b, const uint8_t* blk, int
 // fragment reads free of bank conflicts.
 enum XMode { kFrag = 0, kLines16 = 1, kLines8 = 2 };
 
-template <int FMT, int RG>
+template <int FMT, int RG, bool R8 = false>
 struct XCursor {
   static constexpr int kMode =
-      FMT == FMT_NVFP4 ? kLines8 : ((RG >= 2 || FMT == FMT_NVFP4S) ? kLines16 : kFrag);
+      (FMT == FMT_NVFP4 || R8) ? kLines8 : ((RG >= 2 || FMT == FMT_NVFP4S) ? kLines16 : kFrag);
   static_assert(kMode != kLines8 || RG == 1, "the NVFP4 M <= 8 family has one row group");
   const uint16_t* row[RG];   // fragment mode: the lane's row; line modes: rows 0-7
   const uint16_t* half[RG];  // kLines16: rows 8-15
@@ -480,7 +482,7 @@ struct XStage {
 // wave's LDS area xs. The wave barriers keep the compiler from moving the LDS
 // reads above the writes, or the next call's writes above this call's reads;
 // a wave's LDS operations execute in order.
-template <int MODE, int RG>
+template <int MODE, int RG, int FMT>
 __device__ __forceinline__ void stage_x(const XBuf<RG>& in, XBuf<RG>& out, u32x4_t* xs, int lane) {
   __builtin_amdgcn_wave_barrier();
   constexpr int NC = MODE == kLines8 ? 2 : 4;
@@ -491,7 +493,7 @@ __device__ __forceinline__ void stage_x(const XBuf<RG>& in, XBuf<RG>& out, u32x4
   __builtin_amdgcn_wave_barrier();
   const int i = lane & 15, g = lane >> 4;  // MFMA A operand: row i, k 8 g .. +7 of the step
   if constexpr (MODE == kLines8) {
-    const bool carries = (i >> 3) == (g >> 1);
+    const bool carries = FMT == FMT_NVFP4 ? (i >> 3) == (g >> 1) : i < 8;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int seg = 4 * (j & 1) + g;
@@ -899,10 +901,15 @@ struct Occupancy {
 // arguments preloaded at wave launch, -amdgpu-kernarg-preload-count): the
 // first loads are issued without waiting on a kernel-argument fetch
 // (measured 1 % over the pass). The rest of the parameters follow in p.
-template <int FMT, int EPI, int RG>
-__global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kernel(
+//
+// RGX: the row groups, or 0 for a 16-row kernel (FP8, affine) launched with
+// M <= 8: one row group whose rows 8-15 are padding, so its activation loads
+// read only rows 0-7.
+template <int FMT, int EPI, int RGX>
+__global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_kernel(
     const uint8_t* a_w, const uint16_t* a_x, const uint16_t* a_zeros, int64_t a_total, int32_t a_wgs,
     int32_t a_iters, int32_t a_K, int32_t a_M, GemmParams p) {
+  constexpr int RG = RGX == 0 ? 1 : RGX;
   p.w = a_w;
   p.x = a_x;
   p.zeros = a_zeros;
@@ -919,7 +926,8 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
   constexpr int SLOT = NT * REGS * 64;
   constexpr size_t BLOCK = FMT == FMT_FP8 ? kBlockF8 : kBlockF4;
   __shared__ float lds[4 * SLOT];
-  constexpr int XMODE = XCursor<FMT, RG>::kMode;
+  using XC = XCursor<FMT, RG, RGX == 0>;
+  constexpr int XMODE = XC::kMode;
   constexpr bool LINES = XMODE != kFrag;
   constexpr int XS = XStage<XMODE, RG>::kSize;  // line-mode staging per wave
   __shared__ u32x4_t xstage[LINES ? 4 * XS : 1];
@@ -951,7 +959,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
     auto unit_base = [&](int64_t u) { return p.w + (size_t)((u >> 1) * I) * BLOCK + (size_t)(u & 1) * HALF; };
     int64_t lu = first_tile;  // unit of the next load
     const uint8_t* wnext = ACC ? unit_base(lu) + (size_t)(s - lu * I) * BLOCK : p.w + (size_t)s * BLOCK;
-    XCursor<FMT, RG> xc;
+    XC xc;
     xc.init(p, lane);
     if constexpr (XMODE == kLines8) xstage[q * XS + XStage<XMODE, RG>::kZero] = u32x4_t{0u, 0u, 0u, 0u};
     int xkit = (int)(s - (int64_t)first_tile * I);
@@ -986,7 +994,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RG>::value)) void vq_gemm_kern
     auto compute = [&](int qq) {
       if constexpr (LINES) {
         XBuf<RG> xt;
-        stage_x<XMODE, RG>(xb[qq], xt, xstage + q * XS, lane);
+        stage_x<XMODE, RG, FMT>(xb[qq], xt, xstage + q * XS, lane);
         compute_iter<FMT, RG, NT>(wb[qq], xt, acc);
       } else {
         compute_iter<FMT, RG, NT>(wb[qq], xb[qq], acc);
@@ -1182,8 +1190,15 @@ static int launch_rg(const GemmParams& p, hipStream_t st) {
     (void)rg;  // launch_gemm sends M > 8 to the scaled family
     hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
-  } else {
+  } else if constexpr (FMT == FMT_NVFP4S) {
     if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
+                       p.iters, p.K, p.M, p);
+    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
+                       p.iters, p.K, p.M, p);
+  } else {
+    if (p.M <= 8) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 0>), grid, block, 0, st, p.w, p.x, p.zeros, p.total,
+                       p.wgs, p.iters, p.K, p.M, p);
+    else if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
     else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
                        p.iters, p.K, p.M, p);

@@ -207,13 +207,14 @@ def test_fp8_all_codes_one_hot():
     assert same.all()
 
 
-@pytest.mark.parametrize("m", [32, 24, 17, 16, 9])
+@pytest.mark.parametrize("m", [32, 24, 17, 16, 9, 8, 5])
 def test_wide_rows_one_hot_row_map(m):
     # Row r of X is one-hot at k_r (k_r spread over both 128-B lines of an
     # iteration, every 16-B segment and both row halves of a 16-row group), so
     # Y[r] must be exactly column k_r of the decoded weights: pins which
     # activation row and k reach each MFMA lane when the kernels read whole
-    # lines and reorder them in LDS (scaled NVFP4 at M > 8, FP8 at M > 16).
+    # lines and reorder them in LDS (every NVFP4 and FP8 kernel except FP8 at
+    # M = 9-16), including the two-block A operand of NVFP4 at M <= 8.
     n, k = 96, 256
     ks = [(37 * r + 5) % k for r in range(m)]
     x = np.zeros((m, k), dtype=np.uint16)
