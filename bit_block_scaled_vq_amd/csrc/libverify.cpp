@@ -97,7 +97,6 @@ int32_t check_w(const uint8_t* w, size_t w_bytes, size_t need) {
 
 void bind_workspace(vq::GemmParams& p, const vq::Schedule& s, void* ws) {
   char* base = static_cast<char*>(ws);
-  p.zeros = reinterpret_cast<const uint16_t*>(base + s.off_zero);
   p.partials = reinterpret_cast<float*>(base + s.off_partials);
   p.counters = reinterpret_cast<uint32_t*>(base + s.off_counters);
   p.best = s.off_best ? reinterpret_cast<unsigned long long*>(base + s.off_best) : nullptr;
@@ -155,8 +154,6 @@ Schedule make_schedule(int epi, int32_t n_out, int32_t k) {
   }
   s.wgs = (int32_t)g;
   size_t off = 0;
-  s.off_zero = off;
-  off += 256;
   s.off_partials = off;
   off = align_up(off + (size_t)2 * s.wgs * kSlotFloats * sizeof(float), 256);
   s.off_counters = off;
@@ -373,7 +370,6 @@ int32_t vq_gemm_nvfp4_noalloc(const uint16_t* x, const uint8_t* w, size_t w_byte
   p.N = N;
   p.K = K;
   p.y_f32 = y_dtype == VQ_OUT_F32;
-  p.zeros = reinterpret_cast<const uint16_t*>(sc);
   p.counters = reinterpret_cast<uint32_t*>(sc + vq::kScratchCounters);
   p.partials = reinterpret_cast<float*>(sc + vq::kScratchPartials);
   p.tiles = s.tiles;
@@ -499,7 +495,7 @@ int32_t vq_gemm_fp8_accumulate(const uint16_t* x, const uint8_t* w, size_t w_byt
   p.tiles = s.tiles;
   p.iters = s.iters;
   p.total = s.total;
-  p.wgs = s.wgs;  // no workspace: FP8 rows never read the zero region, and no shares are exchanged
+  p.wgs = s.wgs;  // no workspace: the shares are added into y, none is exchanged
   return launch(vq::FMT_FP8, vq::EPI_ACC, p, stream);
 }
 

@@ -45,7 +45,7 @@ struct Schedule {
   int32_t iters;      // I = K / kIterK
   int64_t total;      // T * I
   int32_t wgs;        // G: stream-K workgroups
-  size_t off_zero, off_partials, off_counters, off_best, off_done, bytes;
+  size_t off_partials, off_counters, off_best, off_done, bytes;
 };
 
 // Tiles of an output of n_out columns: 64 columns per tile, or 32 with the
@@ -69,7 +69,6 @@ struct GemmParams {
   int32_t y_f32;
   int32_t tiles, iters, wgs;
   int64_t total;
-  const uint16_t* zeros;  // 256 bytes the kernels never write (zero-filled with the workspace)
   float* partials;
   uint32_t* counters;
   unsigned long long* best;
@@ -147,12 +146,11 @@ struct GdnParams {
 
 // Device scratch of the allocation-free GEMM entry point: one fixed layout
 // for every shape, so calls of different (N, K, epilogue) can follow each
-// other on it: [256 B zero region][per-tile counters][partial-sum slots].
+// other on it: [per-tile counters][partial-sum slots].
 // Counters start at zero (static storage) and every call leaves the ones it
 // used at zero; the slots need no initial value.
 constexpr int kScratchTiles = 1 << 16;                 // N <= 4,194,304 (2,097,152 with SILU_MUL)
-constexpr size_t kScratchZero = 256;
-constexpr size_t kScratchCounters = kScratchZero;
+constexpr size_t kScratchCounters = 0;
 constexpr size_t kScratchPartials = kScratchCounters + (size_t)kScratchTiles * sizeof(uint32_t);
 constexpr size_t kScratchBytes = kScratchPartials + (size_t)2 * kCUs * kSlotFloats * sizeof(float);
 // This device's copy of the scratch array (looked up once per device); 0 on

@@ -391,62 +391,51 @@ __device__ __forceinline__ void load_w(WBuf<FMT, NT>& b, const uint8_t* blk, int
   }
 }
 
-// X cursor: how each iteration's activation rows reach the MFMA A operands.
-//  kFrag (FP8 and affine at one row group): each load is one MFMA step's A
-//    operand, 16 rows x 64 B, half of 16 cache lines.
-//  kLines16 (the scaled NVFP4 family, and FP8 and affine at two or more
-//    16-row groups): each load reads 8 rows x 128 B, whole lines, half the
-//    line requests per byte; 4 loads per row group.
+// X cursor: each iteration's activation rows are read as whole 128-byte
+// lines (8 rows x 128 B per load instruction, two lines per row and
+// iteration) and put in MFMA A-operand order through the wave's LDS area
+// (stage_x). An A operand for one 32-K step is 16 rows x 64 B: loaded
+// directly it would touch half of 16 lines per instruction, twice the line
+// requests per byte.
+//  kLines16 (16-row groups: the scaled NVFP4 family, FP8 and affine at
+//    M > 8): 4 loads per row group and iteration, rows 0-7 and 8-15 of each
+//    half of the iteration's k range.
 //  kLines8 (M <= 8: the NVFP4 M <= 8 family, and the FP8 and affine kernels
-//    instantiated for at most 8 rows): 2 loads per iteration, the 8 rows x
-//    128 B of each half of the iteration's k range. The NVFP4 A operand holds
-//    the rows twice with zeros in between (rows 0-7 on k-groups 0,1, rows
-//    8-15 on k-groups 2,3; see compute_iter); the 16-row kernels' rows 8-15
-//    are padding. Lanes that hold zeros read a zeroed slot.
-// In the line modes lane l reads row l >> 3 (+ 8 for the second half of a
-// 16-row group), 16-byte segment (l & 7) ^ (l >> 3) of the line, and stage_x
-// puts the fragments in MFMA order through the wave's LDS area, where the
-// lane's 16 bytes land at position l & 7 of that row: the swizzle keeps the
-// fragment reads free of bank conflicts.
-enum XMode { kFrag = 0, kLines16 = 1, kLines8 = 2 };
+//    instantiated for at most 8 rows): 2 loads per iteration, rows 0-7. The
+//    NVFP4 A operand holds the rows twice with zeros in between (rows 0-7 on
+//    k-groups 0,1, rows 8-15 on k-groups 2,3; see compute_iter); the 16-row
+//    kernels' rows 8-15 are padding. Lanes that hold zeros read a zeroed slot.
+// Lane l reads row l >> 3 (+ 8 for the second half of a 16-row group),
+// 16-byte segment (l & 7) ^ (l >> 3) of the line, and its 16 bytes land at
+// position l & 7 of that row in LDS: the swizzle keeps the fragment reads
+// free of bank conflicts.
+enum XMode { kLines16 = 1, kLines8 = 2 };
 
 template <int FMT, int RG, bool R8 = false>
 struct XCursor {
-  static constexpr int kMode =
-      (FMT == FMT_NVFP4 || R8) ? kLines8 : ((RG >= 2 || FMT == FMT_NVFP4S) ? kLines16 : kFrag);
-  static_assert(kMode != kLines8 || RG == 1, "the NVFP4 M <= 8 family has one row group");
-  const uint16_t* row[RG];   // fragment mode: the lane's row; line modes: rows 0-7
+  static constexpr int kMode = (FMT == FMT_NVFP4 || R8) ? kLines8 : kLines16;
+  static_assert(kMode != kLines8 || RG == 1, "at most 8 rows: one row group");
+  const uint16_t* row[RG];   // rows 0-7 of each row group
   const uint16_t* half[RG];  // kLines16: rows 8-15
   __device__ __forceinline__ void init(const GemmParams& p, int lane) {
-    if constexpr (kMode != kFrag) {
-      const int r = lane >> 3, seg = (lane & 7) ^ r;
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-        int m0 = 16 * rg + r, m1 = m0 + 8;
-        m0 = m0 < p.M ? m0 : p.M - 1;  // rows past M are padding: any valid row will do
-        m1 = m1 < p.M ? m1 : p.M - 1;
-        row[rg] = p.x + (size_t)m0 * p.K + 8 * seg;
-        half[rg] = p.x + (size_t)m1 * p.K + 8 * seg;
-      }
-      return;
-    }
-    const int i = lane & 15, g = lane >> 4;
+    const int r = lane >> 3, seg = (lane & 7) ^ r;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      int m = 16 * rg + i;
-      m = m < p.M ? m : p.M - 1;
-      row[rg] = p.x + (size_t)m * p.K + 8 * g;
+      int m0 = 16 * rg + r, m1 = m0 + 8;
+      m0 = m0 < p.M ? m0 : p.M - 1;  // rows past M are padding: any valid row will do
+      m1 = m1 < p.M ? m1 : p.M - 1;
+      row[rg] = p.x + (size_t)m0 * p.K + 8 * seg;
+      half[rg] = p.x + (size_t)m1 * p.K + 8 * seg;
     }
   }
-  // kFrag: b.xa[rg][j] is MFMA step j's A operand. kLines16: b.xa[rg][c]
-  // holds rows 8 (c & 1) .. +7 of k 64 (c >> 1) .. +63. kLines8: b.xa[0][c],
-  // c = 0, 1, holds rows 0-7 of k 64 c .. +63.
+  // kLines16: b.xa[rg][c] holds rows 8 (c & 1) .. +7 of k 64 (c >> 1) .. +63.
+  // kLines8: b.xa[0][c], c = 0, 1, holds rows 0-7 of k 64 c .. +63.
   __device__ __forceinline__ void load(XBuf<RG>& b, int kit) const {
     if constexpr (kMode == kLines8) {
       const uint16_t* lo = row[0] + (size_t)(kit * kIterK);
       b.xa[0][0] = ld16(lo);
       b.xa[0][1] = ld16(lo + 64);
-    } else if constexpr (kMode == kLines16) {
+    } else {
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
         const uint16_t* lo = row[rg] + (size_t)(kit * kIterK);
@@ -456,18 +445,11 @@ struct XCursor {
         b.xa[rg][2] = ld16(lo + 64);
         b.xa[rg][3] = ld16(hi + 64);
       }
-    } else {
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-        const uint16_t* xr = row[rg] + (size_t)(kit * kIterK);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b.xa[rg][j] = ld16(xr + j * 32);
-      }
     }
   }
 };
 
-// Line-mode staging: one chunk per (row group, load) holds 8 rows x 128 B;
+// Activation staging: one chunk per (row group, load) holds 8 rows x 128 B;
 // 1152 B per chunk rather than 1024 puts the two row halves of a fragment
 // read on different banks. kLines8 adds one zeroed 16-byte slot after its two
 // chunks.
@@ -475,10 +457,10 @@ constexpr int kXChunk = 72;  // u32x4 per chunk
 template <int MODE, int RG>
 struct XStage {
   static constexpr int kZero = 2 * kXChunk;  // kLines8: the zero slot
-  static constexpr int kSize = MODE == kLines8 ? 2 * kXChunk + 8 : MODE == kLines16 ? 4 * RG * kXChunk : 0;
+  static constexpr int kSize = MODE == kLines8 ? 2 * kXChunk + 8 : 4 * RG * kXChunk;
 };
 
-// Line-mode registers (see XCursor::load) -> MFMA A operands, through this
+// Whole-line registers (see XCursor::load) -> MFMA A operands, through this
 // wave's LDS area xs. The wave barriers keep the compiler from moving the LDS
 // reads above the writes, or the next call's writes above this call's reads;
 // a wave's LDS operations execute in order.
@@ -866,13 +848,13 @@ __device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int l
 // --------------------------------------------------------------- main kernel
 
 // Iterations in flight per wave. The vector-memory counter retires loads in
-// issue order, so X fragments share the weights' ring (a shallower X ring
-// would cap the weight prefetch at its depth).
+// issue order, so the activation lines share the weights' ring (a shallower
+// activation ring would cap the weight prefetch at its depth).
 template <int FMT, int RG, int NT = kNT>
 struct PipeDepth {
-  // wide row groups: the X ring would spill; scaled NVFP4 with two row groups
-  // keeps 2 (3 and 4 measured slower at M = 24 and 32, with fragment-mode and
-  // with line-mode activation loads).
+  // wide row groups: the activation ring would spill; scaled NVFP4 with two
+  // row groups keeps 2 (3 and 4 measured slower at M = 24 and 32). One row
+  // group: 3 (4 measured slower for NVFP4 M <= 8 and FP8 M <= 8).
   // Half-tile units carry half the weight bytes per iteration: 5 deep at one
   // row group (4 and 6 measured slower on 5,120 x 6,144 at M = 8).
   static constexpr int value = NT < kNT ? (RG == 1 ? 5 : 3)
@@ -907,12 +889,11 @@ struct Occupancy {
 // read only rows 0-7.
 template <int FMT, int EPI, int RGX>
 __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_kernel(
-    const uint8_t* a_w, const uint16_t* a_x, const uint16_t* a_zeros, int64_t a_total, int32_t a_wgs,
+    const uint8_t* a_w, const uint16_t* a_x, int64_t a_total, int32_t a_wgs,
     int32_t a_iters, int32_t a_K, int32_t a_M, GemmParams p) {
   constexpr int RG = RGX == 0 ? 1 : RGX;
   p.w = a_w;
   p.x = a_x;
-  p.zeros = a_zeros;
   p.total = a_total;
   p.wgs = a_wgs;
   p.iters = a_iters;
@@ -928,9 +909,8 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_ker
   __shared__ float lds[4 * SLOT];
   using XC = XCursor<FMT, RG, RGX == 0>;
   constexpr int XMODE = XC::kMode;
-  constexpr bool LINES = XMODE != kFrag;
-  constexpr int XS = XStage<XMODE, RG>::kSize;  // line-mode staging per wave
-  __shared__ u32x4_t xstage[LINES ? 4 * XS : 1];
+  constexpr int XS = XStage<XMODE, RG>::kSize;  // activation staging per wave
+  __shared__ u32x4_t xstage[4 * XS];
 
   const int lane = threadIdx.x & 63;
   const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -992,13 +972,9 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_ker
     bool started_inside = ckit != 0;
 
     auto compute = [&](int qq) {
-      if constexpr (LINES) {
-        XBuf<RG> xt;
-        stage_x<XMODE, RG, FMT>(xb[qq], xt, xstage + q * XS, lane);
-        compute_iter<FMT, RG, NT>(wb[qq], xt, acc);
-      } else {
-        compute_iter<FMT, RG, NT>(wb[qq], xb[qq], acc);
-      }
+      XBuf<RG> xt;
+      stage_x<XMODE, RG, FMT>(xb[qq], xt, xstage + q * XS, lane);
+      compute_iter<FMT, RG, NT>(wb[qq], xt, acc);
     };
 
     auto tile_end = [&]() {
@@ -1188,19 +1164,19 @@ static int launch_rg(const GemmParams& p, hipStream_t st) {
   const dim3 grid((unsigned)p.wgs), block(256);
   if constexpr (FMT == FMT_NVFP4) {
     (void)rg;  // launch_gemm sends M > 8 to the scaled family
-    hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
+    hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
   } else if constexpr (FMT == FMT_NVFP4S) {
-    if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
+    if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
-    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
+    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
   } else {
-    if (p.M <= 8) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 0>), grid, block, 0, st, p.w, p.x, p.zeros, p.total,
+    if (p.M <= 8) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 0>), grid, block, 0, st, p.w, p.x, p.total,
                        p.wgs, p.iters, p.K, p.M, p);
-    else if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
+    else if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
-    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p.w, p.x, p.zeros, p.total, p.wgs,
+    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
   }
   return (int)hipGetLastError();
