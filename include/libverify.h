@@ -157,8 +157,8 @@ int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* w, size_t w_bytes,
  * harnesses that forbid hipMalloc). Arguments, results and rounding are those
  * of vq_gemm_nvfp4 (the same kernels and split-K schedule, so the outputs are
  * bitwise equal); the partial sums and per-tile counters live in a static
- * device array of the library, one per device, 256 B + 256 KiB + 8 MiB
- * (8,651,008 bytes), allocated when the library's code is loaded on the device
+ * device array of the library, one per device, 256 KiB + 8 MiB
+ * (8,650,752 bytes), allocated when the library's code is loaded on the device
  * and held until the process ends. Limits: N <= 4,194,304 output columns
  * (2,097,152 with VQ_EPI_SILU_MUL); larger N returns VQ_ERR_SHAPE. Every call
  * on a device shares that device's array and leaves its counters at zero, so
