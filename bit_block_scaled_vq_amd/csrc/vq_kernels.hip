@@ -42,7 +42,11 @@
 //    accumulated in fp32.
 //  * Weights stream with non-temporal 16-byte loads, 3 iterations in flight
 //    per wave; one workgroup of 4 waves per CU, registers budgeted for one
-//    wave per SIMD.
+//    wave per SIMD. The activation rows of an iteration are read as whole
+//    128-byte lines (8 rows x 128 B per load) in the same ring and put in
+//    A-operand order through a small LDS area of the wave; at M <= 8 only
+//    rows 0-7 are read (an 8-row instance of the 16-row FP8 and affine
+//    kernels).
 //  * Stream-K over 4-wave workgroups: workgroup g owns iterations
 //    [g*W/G, (g+1)*W/G) of the (tile, iteration) space and each wave a
 //    contiguous quarter of that. Tiles shared by waves of one workgroup are
