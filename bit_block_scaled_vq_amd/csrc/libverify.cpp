@@ -102,6 +102,7 @@ void bind_workspace(vq::GemmParams& p, const vq::Schedule& s, void* ws) {
   p.best = s.off_best ? reinterpret_cast<unsigned long long*>(base + s.off_best) : nullptr;
   p.done = s.off_done ? reinterpret_cast<uint32_t*>(base + s.off_done) : nullptr;
   p.tiles = s.tiles;
+  p.unit_subs = s.unit_subs;
   p.iters = s.iters;
   p.total = s.total;
   p.wgs = s.wgs;
@@ -117,9 +118,12 @@ int32_t launch(int fmt, int epi, const vq::GemmParams& p, void* stream) {
 
 namespace vq {
 
-Schedule make_schedule(int epi, int32_t n_out, int32_t k) {
+Schedule make_schedule(int epi, int32_t n_out, int32_t k, bool wide_rows) {
   Schedule s{};
-  s.tiles = tiles_for(epi, n_out);
+  const int32_t tiles = tiles_for(epi, n_out);
+  const bool pairs = wide_rows && epi != EPI_ACC && tiles >= kPairMinTiles;
+  s.unit_subs = epi == EPI_ACC ? kNT / 2 : (pairs ? 2 * kNT : kNT);
+  s.tiles = pairs ? (tiles + 1) / 2 : tiles;
   s.iters = k / kIterK;
   s.total = (int64_t)s.tiles * s.iters;
   // Stream-K over at most kMaxWgs 4-wave workgroups, each wave with at least
@@ -157,7 +161,9 @@ Schedule make_schedule(int epi, int32_t n_out, int32_t k) {
   s.off_partials = off;
   off = align_up(off + (size_t)2 * s.wgs * kSlotFloats * sizeof(float), 256);
   s.off_counters = off;
-  off = align_up(off + (size_t)s.tiles * sizeof(uint32_t), 256);
+  // one counter per tile, whatever the unit: both NVFP4 families lay out a
+  // workspace of (op, N, K) the same way when their workgroup counts agree
+  off = align_up(off + (size_t)tiles * sizeof(uint32_t), 256);
   if (epi == EPI_ARGMAX) {
     s.off_best = off;
     off = align_up(off + (size_t)kBuckets * kMaxRows * sizeof(unsigned long long), 256);
@@ -214,13 +220,19 @@ size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K) {
     return vq::make_sample_layout(M, N).bytes;
   }
   if (!shape_ok(M, N, K)) return 0;
+  // NVFP4 ops: large enough for both families (M <= 8 and M > 8), so one
+  // workspace of (op, N, K) serves every M
+  auto both = [&](int epi) {
+    const size_t a = vq::make_schedule(epi, N, K, false).bytes, b = vq::make_schedule(epi, N, K, true).bytes;
+    return a > b ? a : b;
+  };
   switch (op) {
-    case VQ_OP_NVFP4: return vq::make_schedule(vq::EPI_NONE, N, K).bytes;
+    case VQ_OP_NVFP4: return both(vq::EPI_NONE);
     case VQ_OP_NVFP4_SILU_MUL:
       if (N > (1 << 29)) return 0;
-      return vq::make_schedule(vq::EPI_SILU, N, K).bytes;
+      return both(vq::EPI_SILU);
     case VQ_OP_FP8: return vq::make_schedule(vq::EPI_NONE, N, K).bytes;
-    case VQ_OP_LMHEAD: return vq::make_schedule(vq::EPI_ARGMAX, N, K).bytes;
+    case VQ_OP_LMHEAD: return both(vq::EPI_ARGMAX);
     case VQ_OP_AFFINE_Q4: return vq::make_schedule(vq::EPI_NONE, N, K).bytes;
     case VQ_OP_AFFINE_Q4_SILU_MUL:
       if (N > (1 << 29)) return 0;
@@ -231,18 +243,22 @@ size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K) {
 
 size_t vq_packed_bytes(int32_t kind, int32_t rows, int32_t K) { return packed_bytes(kind, rows, K); }
 
-int32_t vq_schedule_info(int32_t op, int32_t N, int32_t K, int32_t* units, int32_t* iters, int32_t* workgroups) {
+int32_t vq_schedule_info(int32_t op, int32_t M, int32_t N, int32_t K, int32_t* units, int32_t* iters,
+                         int32_t* workgroups) {
   if (!units || !iters || !workgroups) return fail(VQ_ERR_NULL, "vq_schedule_info: outputs are required");
-  if (!shape_ok(8, N, K)) return fail(VQ_ERR_SHAPE, "vq_schedule_info: N = %d, K = %d out of range", N, K);
+  if (!shape_ok(M, N, K)) return fail(VQ_ERR_SHAPE, "vq_schedule_info: M = %d, N = %d, K = %d out of range", M, N, K);
   int epi;
+  bool nvfp4 = false;
   switch (op) {
-    case VQ_OP_NVFP4: case VQ_OP_FP8: case VQ_OP_AFFINE_Q4: epi = vq::EPI_NONE; break;
-    case VQ_OP_NVFP4_SILU_MUL: case VQ_OP_AFFINE_Q4_SILU_MUL: epi = vq::EPI_SILU; break;
-    case VQ_OP_LMHEAD: epi = vq::EPI_ARGMAX; break;
+    case VQ_OP_NVFP4: nvfp4 = true; epi = vq::EPI_NONE; break;
+    case VQ_OP_FP8: case VQ_OP_AFFINE_Q4: epi = vq::EPI_NONE; break;
+    case VQ_OP_NVFP4_SILU_MUL: nvfp4 = true; epi = vq::EPI_SILU; break;
+    case VQ_OP_AFFINE_Q4_SILU_MUL: epi = vq::EPI_SILU; break;
+    case VQ_OP_LMHEAD: nvfp4 = true; epi = vq::EPI_ARGMAX; break;
     case VQ_OP_FP8_ACCUMULATE: epi = vq::EPI_ACC; break;
     default: return fail(VQ_ERR_VALUE, "vq_schedule_info: op %d has no GEMM schedule", op);
   }
-  const vq::Schedule s = vq::make_schedule(epi, N, K);
+  const vq::Schedule s = vq::make_schedule(epi, N, K, nvfp4 && M > 8);
   *units = s.tiles;
   *iters = s.iters;
   *workgroups = s.wgs;
@@ -316,7 +332,7 @@ int32_t vq_gemm_nvfp4(const uint16_t* x, const uint8_t* w, size_t w_bytes, float
                                  : packed_bytes(VQ_PACK_NVFP4, N, K));
   if (st) return st;
   const int epi = silu ? vq::EPI_SILU : vq::EPI_NONE;
-  const vq::Schedule s = vq::make_schedule(epi, N, K);
+  const vq::Schedule s = vq::make_schedule(epi, N, K, M > 8);
   st = check_ws(s, workspace, workspace_bytes);
   if (st) return st;
   st = check_device();
@@ -352,7 +368,7 @@ int32_t vq_gemm_nvfp4_noalloc(const uint16_t* x, const uint8_t* w, size_t w_byte
   st = check_w(w, w_bytes, silu ? packed_bytes(VQ_PACK_NVFP4_GATE_UP, 2 * (int64_t)N, K)
                                  : packed_bytes(VQ_PACK_NVFP4, N, K));
   if (st) return st;
-  const vq::Schedule s = vq::make_schedule(epi, N, K);
+  const vq::Schedule s = vq::make_schedule(epi, N, K, M > 8);
   if (s.wgs > vq::kCUs) return fail(VQ_ERR_SHAPE, "schedule of %d workgroups exceeds the scratch's %d", s.wgs, vq::kCUs);
   st = check_device();
   if (st) return st;
@@ -373,6 +389,7 @@ int32_t vq_gemm_nvfp4_noalloc(const uint16_t* x, const uint8_t* w, size_t w_byte
   p.counters = reinterpret_cast<uint32_t*>(sc + vq::kScratchCounters);
   p.partials = reinterpret_cast<float*>(sc + vq::kScratchPartials);
   p.tiles = s.tiles;
+  p.unit_subs = s.unit_subs;
   p.iters = s.iters;
   p.total = s.total;
   p.wgs = s.wgs;
@@ -493,6 +510,7 @@ int32_t vq_gemm_fp8_accumulate(const uint16_t* x, const uint8_t* w, size_t w_byt
   p.K = K;
   p.y_f32 = 1;
   p.tiles = s.tiles;
+  p.unit_subs = s.unit_subs;
   p.iters = s.iters;
   p.total = s.total;
   p.wgs = s.wgs;  // no workspace: the shares are added into y, none is exchanged
@@ -522,7 +540,7 @@ int32_t vq_lmhead_argmax_accept(const uint16_t* h, const uint8_t* w, size_t w_by
     return fail(VQ_ERR_ALIGN, "logits_out is not aligned to its element size");
   st = check_w(w, w_bytes, packed_bytes(VQ_PACK_NVFP4, V, K));
   if (st) return st;
-  const vq::Schedule s = vq::make_schedule(vq::EPI_ARGMAX, V, K);
+  const vq::Schedule s = vq::make_schedule(vq::EPI_ARGMAX, V, K, M > 8);
   st = check_ws(s, workspace, workspace_bytes);
   if (st) return st;
   st = check_device();

@@ -41,10 +41,11 @@ constexpr int kBuckets = 64;
 constexpr int kMaxRows = 32;
 
 struct Schedule {
-  int32_t tiles;      // T
+  int32_t tiles;      // T: units of the schedule (tiles, half tiles or tile pairs)
   int32_t iters;      // I = K / kIterK
   int64_t total;      // T * I
   int32_t wgs;        // G: stream-K workgroups
+  int32_t unit_subs;  // sub-tiles per unit: 2 (half tiles), 4 (tiles), 8 (tile pairs)
   size_t off_partials, off_counters, off_best, off_done, bytes;
 };
 
@@ -57,8 +58,16 @@ inline int32_t tiles_for(int epi, int32_t n_out) {
   return (n_out + cols - 1) / cols;
 }
 
-// The schedule depends only on (epilogue kind, N, K), never on M.
-Schedule make_schedule(int epi, int32_t n_out, int32_t k);
+// Tile pairs as units for the scaled NVFP4 family (M > 8) from this many
+// tiles on: one activation load then feeds 128 output columns. Only where a
+// workgroup gets many units: the vocabulary head (3,880 tiles) at M = 32
+// 160 against 180 us per launch, but [gate; up] (544 tiles, 1.1 pairs per
+// workgroup, nearly every pair then split between two) 38.3 against 34.2 us.
+constexpr int32_t kPairMinTiles = 8 * kCUs;
+
+// The schedule depends only on (epilogue kind, N, K) and on wide_rows, the
+// scaled NVFP4 family (NVFP4 at M > 8), never on M otherwise.
+Schedule make_schedule(int epi, int32_t n_out, int32_t k, bool wide_rows = false);
 
 struct GemmParams {
   const uint16_t* x;
@@ -67,7 +76,8 @@ struct GemmParams {
   void* y;
   int32_t M, N, K;        // N: output columns
   int32_t y_f32;
-  int32_t tiles, iters, wgs;
+  int32_t tiles, iters, wgs;  // tiles: units of the schedule
+  int32_t unit_subs;          // sub-tiles per unit (the kernel instance's NT)
   int64_t total;
   float* partials;
   uint32_t* counters;

@@ -333,12 +333,9 @@ __device__ __forceinline__ int out_col(int tile, int t, int n) {
   return tile * kTileRows + t * kSub + n;
 }
 
-// Sub-tiles per unit of the (unit, iteration) space: a whole 64-row tile, or
-// half of one (two sub-tiles) for the accumulating epilogue.
-template <int EPI>
-struct UnitSubs {
-  static constexpr int value = EPI == EPI_ACC ? kNT / 2 : kNT;
-};
+// Sub-tiles per unit of the (unit, iteration) space (the kernel's NT): a
+// whole 64-row tile (4), half of one for the accumulating epilogue (2), or a
+// pair of tiles for the scaled NVFP4 family on wide outputs (8).
 
 // ---------------------------------------------------------- per-iteration data
 
@@ -348,9 +345,18 @@ template <>
 struct WBuf<FMT_NVFP4, kNT> {
   u32x4_t c[kNT];  // per sub-tile: code dwords of MFMA steps 0..3
   u32x4_t s;       // per sub-tile: the 4 block scales of this lane's half
+  __device__ __forceinline__ uint32_t scales(int t) const { return s[t]; }
 };
 template <>
 struct WBuf<FMT_NVFP4S, kNT> : WBuf<FMT_NVFP4, kNT> {};
+// A tile pair (scaled NVFP4 at M > 8 on wide outputs): the two tiles' blocks
+// of one iteration, sub-tiles 0-3 from the first tile and 4-7 from the second.
+template <>
+struct WBuf<FMT_NVFP4S, 2 * kNT> {
+  u32x4_t c[2 * kNT];
+  u32x4_t s[2];
+  __device__ __forceinline__ uint32_t scales(int t) const { return s[t >> 2][t & 3]; }
+};
 template <>
 struct WBuf<FMT_AFFINE, kNT> {
   u32x4_t c[kNT];   // per sub-tile: code dwords of MFMA steps 0..3
@@ -373,11 +379,19 @@ __device__ __forceinline__ u32x4_t ldnt(const void* p) {
 }
 
 // blk: the block, or for a half-tile unit (NT = 2, FP8 only) the start of the
-// half's two sub-tiles inside its block.
+// half's two sub-tiles inside its block; blk2: a tile pair's second block.
 template <int FMT, int NT>
-__device__ __forceinline__ void load_w(WBuf<FMT, NT>& b, const uint8_t* blk, int lane) {
-  static_assert(NT == kNT || FMT == FMT_FP8, "half-tile units are FP8 only");
-  if constexpr (FMT == FMT_AFFINE) {
+__device__ __forceinline__ void load_w(WBuf<FMT, NT>& b, const uint8_t* blk, const uint8_t* blk2, int lane) {
+  static_assert(NT == kNT || (NT < kNT && FMT == FMT_FP8) || (NT > kNT && FMT == FMT_NVFP4S),
+                "half-tile units are FP8 only, tile pairs scaled NVFP4 only");
+  if constexpr (NT > kNT) {
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) b.c[t] = ldnt(blk + t * 1024 + lane * 16);
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) b.c[kNT + t] = ldnt(blk2 + t * 1024 + lane * 16);
+    b.s[0] = ldnt(blk + 4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
+    b.s[1] = ldnt(blk2 + 4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
+  } else if constexpr (FMT == FMT_AFFINE) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) b.c[t] = ldnt(blk + t * 1024 + lane * 16);
     b.sb[0] = ldnt(blk + 4096 + (lane & 15) * 32);
@@ -539,7 +553,7 @@ __device__ __forceinline__ void compute_iter(const WBuf<FMT, NT>& b, const XBuf<
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float sc = scale_byte(b.s[t], j);
+        const float sc = scale_byte(b.scales(t), j);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc.v[t][r] = __builtin_fmaf(sc, d[t][j][r], acc.v[t][r]);
       }
@@ -548,7 +562,7 @@ __device__ __forceinline__ void compute_iter(const WBuf<FMT, NT>& b, const XBuf<
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8_t wv = dec_fp4x8_scaled(b.c[t][j], scale_byte(b.s[t], j));
+        const bf16x8_t wv = dec_fp4x8_scaled(b.c[t][j], scale_byte(b.scales(t), j));
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
           f32x4_t a = {acc.v[t][4 * rg], acc.v[t][4 * rg + 1], acc.v[t][4 * rg + 2], acc.v[t][4 * rg + 3]};
@@ -686,7 +700,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int tile, int lane
         if (m < p.M) {
           float* y = static_cast<float*>(p.y);
 #pragma unroll
-          for (int t = 0; t < UnitSubs<EPI>::value; ++t) {
+          for (int t = 0; t < kNT / 2; ++t) {
             const int col = out_col<EPI>(tile, t, n);
             if (col < p.N)
               __hip_atomic_fetch_add(y + (size_t)m * p.N + col, get(t, q) * sc, __ATOMIC_RELAXED,
@@ -725,6 +739,19 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int tile, int lane
         }
       }
     }
+  }
+}
+
+// Epilogue of a finished unit: its tile, its half tile (accumulating), or both
+// tiles of a pair. A pair's second tile past the last one (an odd tile count)
+// has only columns >= N, which the epilogue skips.
+template <int FMT, int EPI, int RG, int NT, typename GetF>
+__device__ __forceinline__ void unit_epilogue(const GemmParams& p, int unit, int lane, GetF get, Best<4 * RG>& best) {
+  if constexpr (NT > kNT) {
+    epilogue<FMT, EPI, RG>(p, 2 * unit, lane, get, best);
+    epilogue<FMT, EPI, RG>(p, 2 * unit + 1, lane, [&](int t, int r) { return get(kNT + t, r); }, best);
+  } else {
+    epilogue<FMT, EPI, RG>(p, unit, lane, get, best);
   }
 }
 
@@ -783,13 +810,13 @@ __device__ __forceinline__ void lds_add(const float* slot, int lane, float (&v)[
     for (int r = 0; r < REGS; ++r) v[t][r] += slot[(t * REGS + r) * 64 + lane];
 }
 
-template <int FMT, int REGS>
-__device__ __forceinline__ void store_piece(const GemmParams& p, int64_t slot, int lane, const float (&v)[kNT][REGS]) {
-  static_assert(kNT * REGS * 64 <= kSlotFloats, "slot too small");
+template <int FMT, int REGS, int NT>
+__device__ __forceinline__ void store_piece(const GemmParams& p, int64_t slot, int lane, const float (&v)[NT][REGS]) {
+  static_assert(NT * REGS * 64 <= kSlotFloats, "slot too small");
   if (!holds_sum<FMT>(lane)) return;
   float* dst = p.partials + slot * kSlotFloats;
 #pragma unroll
-  for (int t = 0; t < kNT; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < REGS; ++r)
       __hip_atomic_store(&dst[(t * REGS + r) * 64 + lane], v[t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -810,26 +837,26 @@ __device__ __forceinline__ bool arrive(const GemmParams& p, int tile, int lane) 
 // Workgroups after the first start inside the tile (their slot 0); the first
 // one holds the tile in slot 0 only if it starts exactly at the tile's start.
 // Up to B pieces are loaded per step (one round trip for the usual 2-4).
-template <int FMT, int REGS>
-__device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int lane, float (&sum)[kNT][REGS]) {
+template <int FMT, int REGS, int NT>
+__device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int lane, float (&sum)[NT][REGS]) {
   const int64_t t0 = (int64_t)tile * p.iters;
   const int64_t g0 = wg_of(t0, p), g1 = wg_of(t0 + p.iters - 1, p);
 #pragma unroll
-  for (int t = 0; t < kNT; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < REGS; ++r) sum[t][r] = 0.0f;
   if (holds_sum<FMT>(lane)) {
     const int64_t first_slot = 2 * g0 + (wg_start(g0, p) == t0 ? 0 : 1);
-    constexpr int B = REGS <= 4 ? 4 : 2;
+    constexpr int B = NT * REGS <= 16 ? 4 : 2;
     for (int64_t gb = g0; gb <= g1; gb += B) {
-      float v[B][kNT][REGS];
+      float v[B][NT][REGS];
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         if (gb + b <= g1) {  // uniform
           const int64_t gg = gb + b;
           const float* a = p.partials + (gg == g0 ? first_slot : 2 * gg) * kSlotFloats;
 #pragma unroll
-          for (int t = 0; t < kNT; ++t)
+          for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < REGS; ++r)
               v[b][t][r] = __hip_atomic_load(&a[(t * REGS + r) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -839,7 +866,7 @@ __device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int l
       for (int b = 0; b < B; ++b) {
         if (gb + b <= g1) {
 #pragma unroll
-          for (int t = 0; t < kNT; ++t)
+          for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < REGS; ++r) sum[t][r] += v[b][t][r];
         }
@@ -860,7 +887,8 @@ struct PipeDepth {
   // row groups keeps 2 (3 and 4 measured slower at M = 24 and 32). One row
   // group: 3 (4 measured slower for NVFP4 M <= 8 and FP8 M <= 8).
   // Half-tile units carry half the weight bytes per iteration: 5 deep at one
-  // row group (4 and 6 measured slower on 5,120 x 6,144 at M = 8).
+  // row group (4 and 6 measured slower on 5,120 x 6,144 at M = 8). Tile pairs
+  // keep the tiles' depths (twice the weight bytes per slot).
   static constexpr int value = NT < kNT ? (RG == 1 ? 5 : 3)
                                         : (FMT == FMT_NVFP4S && RG == 2) ? 2 : (RG <= 2 ? 3 : 2);
 };
@@ -890,8 +918,9 @@ struct Occupancy {
 //
 // RGX: the row groups, or 0 for a 16-row kernel (FP8, affine) launched with
 // M <= 8: one row group whose rows 8-15 are padding, so its activation loads
-// read only rows 0-7.
-template <int FMT, int EPI, int RGX>
+// read only rows 0-7. NT: sub-tiles per unit of the schedule (2: half tiles of
+// the accumulating epilogue; 4: tiles; 8: tile pairs, scaled NVFP4 only).
+template <int FMT, int EPI, int RGX, int NT>
 __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_kernel(
     const uint8_t* a_w, const uint16_t* a_x, int64_t a_total, int32_t a_wgs,
     int32_t a_iters, int32_t a_K, int32_t a_M, GemmParams p) {
@@ -904,8 +933,9 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_ker
   p.K = a_K;
   p.M = a_M;
   using T = Traits<FMT, RG>;
-  constexpr int NT = UnitSubs<EPI>::value;
   constexpr bool ACC = EPI == EPI_ACC;
+  static_assert(ACC == (NT < kNT), "half-tile units are the accumulating epilogue's");
+  constexpr bool JUMP = NT != kNT;  // a unit's stream is not the next run of blocks
   constexpr int PD = PipeDepth<FMT, RG, NT>::value;
   constexpr int REGS = T::REGS;
   constexpr int SLOT = NT * REGS * 64;
@@ -936,13 +966,19 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_ker
   acc.zero();
 
   if (s < e) {
-    // The wave's weight stream is the contiguous run of blocks [s, e); with
+    // The wave's weight stream is the contiguous run of blocks [s, e). With
     // half-tile units, unit u is half u & 1 of tile u >> 1 and its stream the
-    // first or second half of each of that tile's blocks.
+    // first or second half of each of that tile's blocks; with tile pairs,
+    // unit u is tiles 2u and 2u + 1, streamed side by side (the second one
+    // re-reads the first where the tile count is odd and 2u + 1 is past it).
     constexpr size_t HALF = BLOCK / 2;  // FP8: sub-tiles 2 and 3 fill the second half of a block
-    auto unit_base = [&](int64_t u) { return p.w + (size_t)((u >> 1) * I) * BLOCK + (size_t)(u & 1) * HALF; };
+    auto unit_base = [&](int64_t u) {
+      if constexpr (NT < kNT) return p.w + (size_t)((u >> 1) * I) * BLOCK + (size_t)(u & 1) * HALF;
+      else return p.w + (size_t)(u * (NT / kNT) * I) * BLOCK;
+    };
+    const int ptiles = EPI == EPI_SILU ? (p.N + kSub * 2 - 1) / (kSub * 2) : (p.N + kTileRows - 1) / kTileRows;
     int64_t lu = first_tile;  // unit of the next load
-    const uint8_t* wnext = ACC ? unit_base(lu) + (size_t)(s - lu * I) * BLOCK : p.w + (size_t)s * BLOCK;
+    const uint8_t* wnext = unit_base(lu) + (size_t)(s - lu * I) * BLOCK;
     XC xc;
     xc.init(p, lane);
     if constexpr (XMODE == kLines8) xstage[q * XS + XStage<XMODE, RG>::kZero] = u32x4_t{0u, 0u, 0u, 0u};
@@ -952,11 +988,13 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_ker
     WBuf<FMT, NT> wb[PD];
     XBuf<RG> xb[PD];
     auto load_next = [&](int qq) {
-      load_w<FMT, NT>(wb[qq], wnext, lane);
+      const uint8_t* wpair = wnext;
+      if constexpr (NT > kNT) wpair = 2 * lu + 1 < ptiles ? wnext + (size_t)I * BLOCK : wnext;
+      load_w<FMT, NT>(wb[qq], wnext, wpair, lane);
       xc.load(xb[qq], xkit);
       if (lit + 1 < e) {  // loads past the range re-read the last iteration
         ++lit;
-        if constexpr (ACC) {
+        if constexpr (JUMP) {
           if (++xkit == I) {
             xkit = 0;
             wnext = unit_base(++lu);
@@ -984,7 +1022,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_ker
     auto tile_end = [&]() {
       acc.combine();
       if (!started_inside) {
-        epilogue<FMT, EPI, RG>(p, ctile, lane, [&](int t, int r) { return acc.get(t, r); }, best);
+        unit_epilogue<FMT, EPI, RG, NT>(p, ctile, lane, [&](int t, int r) { return acc.get(t, r); }, best);
         ++finished;
       } else {
         lds_put<FMT, REGS, NT>(lds + q * SLOT, lane, acc.v);
@@ -1041,17 +1079,17 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_ker
   auto finish = [&](int tile, float (&sum)[NT][REGS]) {
     const int64_t t0 = (int64_t)tile * I;
     if (ACC || (t0 >= S && t0 + I <= E)) {  // accumulating: every share is added, no exchange
-      epilogue<FMT, EPI, RG>(p, tile, lane, [&](int t, int r) { return sum[t][r]; }, best);
+      unit_epilogue<FMT, EPI, RG, NT>(p, tile, lane, [&](int t, int r) { return sum[t][r]; }, best);
       ++finished;
       return;
     }
     if constexpr (!ACC) {
-    store_piece<FMT, REGS>(p, 2 * g + (tile == S / I ? 0 : 1), lane, sum);
+    store_piece<FMT, REGS, NT>(p, 2 * g + (tile == S / I ? 0 : 1), lane, sum);
     wait_stores();
     if (arrive(p, tile, lane)) {
-      float tot[kNT][REGS];
-      reduce_tile<FMT, REGS>(p, tile, lane, tot);
-      epilogue<FMT, EPI, RG>(p, tile, lane, [&](int t, int r) { return tot[t][r]; }, best);
+      float tot[NT][REGS];
+      reduce_tile<FMT, REGS, NT>(p, tile, lane, tot);
+      unit_epilogue<FMT, EPI, RG, NT>(p, tile, lane, [&](int t, int r) { return tot[t][r]; }, best);
       ++finished;
     }
     }
@@ -1161,26 +1199,26 @@ int scratch_ptr(void** out) {
 
 // ---------------------------------------------------------------- launchers
 
-template <int FMT, int EPI>
+template <int FMT, int EPI, int NT>
 static int launch_rg(const GemmParams& p, hipStream_t st) {
   const int rows = FMT == FMT_NVFP4 ? 8 : 16;
   const int rg = (p.M + rows - 1) / rows;
   const dim3 grid((unsigned)p.wgs), block(256);
   if constexpr (FMT == FMT_NVFP4) {
     (void)rg;  // launch_gemm sends M > 8 to the scaled family
-    hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
+    hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
   } else if constexpr (FMT == FMT_NVFP4S) {
-    if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
+    if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
-    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
+    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
   } else {
-    if (p.M <= 8) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 0>), grid, block, 0, st, p.w, p.x, p.total,
+    if (p.M <= 8) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 0, NT>), grid, block, 0, st, p.w, p.x, p.total,
                        p.wgs, p.iters, p.K, p.M, p);
-    else if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
+    else if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
-    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
+    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
   }
   return (int)hipGetLastError();
@@ -1189,22 +1227,28 @@ static int launch_rg(const GemmParams& p, hipStream_t st) {
 int launch_gemm(int fmt, int epi, const GemmParams& p, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (fmt == FMT_NVFP4 && p.M > 8) {
-    // more than 8 rows: scale in registers, 16 activation rows per MFMA
-    if (epi == EPI_NONE) return launch_rg<FMT_NVFP4S, EPI_NONE>(p, st);
-    if (epi == EPI_SILU) return launch_rg<FMT_NVFP4S, EPI_SILU>(p, st);
-    return launch_rg<FMT_NVFP4S, EPI_ARGMAX>(p, st);
+    // more than 8 rows: scale in registers, 16 activation rows per MFMA; the
+    // schedule's units are tiles or, on wide outputs, tile pairs
+    if (p.unit_subs != kNT && p.unit_subs != 2 * kNT) return (int)hipErrorInvalidValue;
+    const bool pair = p.unit_subs == 2 * kNT;
+    if (epi == EPI_NONE)
+      return pair ? launch_rg<FMT_NVFP4S, EPI_NONE, 2 * kNT>(p, st) : launch_rg<FMT_NVFP4S, EPI_NONE, kNT>(p, st);
+    if (epi == EPI_SILU)
+      return pair ? launch_rg<FMT_NVFP4S, EPI_SILU, 2 * kNT>(p, st) : launch_rg<FMT_NVFP4S, EPI_SILU, kNT>(p, st);
+    return pair ? launch_rg<FMT_NVFP4S, EPI_ARGMAX, 2 * kNT>(p, st) : launch_rg<FMT_NVFP4S, EPI_ARGMAX, kNT>(p, st);
   }
+  if (p.unit_subs != (epi == EPI_ACC ? kNT / 2 : kNT)) return (int)hipErrorInvalidValue;
   if (fmt == FMT_NVFP4) {
-    if (epi == EPI_NONE) return launch_rg<FMT_NVFP4, EPI_NONE>(p, st);
-    if (epi == EPI_SILU) return launch_rg<FMT_NVFP4, EPI_SILU>(p, st);
-    return launch_rg<FMT_NVFP4, EPI_ARGMAX>(p, st);
+    if (epi == EPI_NONE) return launch_rg<FMT_NVFP4, EPI_NONE, kNT>(p, st);
+    if (epi == EPI_SILU) return launch_rg<FMT_NVFP4, EPI_SILU, kNT>(p, st);
+    return launch_rg<FMT_NVFP4, EPI_ARGMAX, kNT>(p, st);
   }
   if (fmt == FMT_AFFINE) {
-    if (epi == EPI_SILU) return launch_rg<FMT_AFFINE, EPI_SILU>(p, st);
-    return launch_rg<FMT_AFFINE, EPI_NONE>(p, st);
+    if (epi == EPI_SILU) return launch_rg<FMT_AFFINE, EPI_SILU, kNT>(p, st);
+    return launch_rg<FMT_AFFINE, EPI_NONE, kNT>(p, st);
   }
-  if (epi == EPI_ACC) return launch_rg<FMT_FP8, EPI_ACC>(p, st);
-  return launch_rg<FMT_FP8, EPI_NONE>(p, st);
+  if (epi == EPI_ACC) return launch_rg<FMT_FP8, EPI_ACC, kNT / 2>(p, st);
+  return launch_rg<FMT_FP8, EPI_NONE, kNT>(p, st);
 }
 
 int launch_pack(int fmt, const PackParams& p, void* stream) {

@@ -97,7 +97,7 @@ def lib() -> ctypes.CDLL:
     L.vq_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.vq_workspace_bytes.restype = sz
     pi = ctypes.POINTER(i32)
-    L.vq_schedule_info.argtypes = [i32, i32, i32, pi, pi, pi]
+    L.vq_schedule_info.argtypes = [i32, i32, i32, i32, pi, pi, pi]
     L.vq_schedule_info.restype = i32
     L.vq_status_str.argtypes = [i32]
     L.vq_status_str.restype = ctypes.c_char_p
@@ -164,10 +164,11 @@ def workspace_bytes(op: int, M: int, N: int, K: int) -> int:
     return int(lib().vq_workspace_bytes(op, M, N, K))
 
 
-def schedule_info(op: int, N: int, K: int):
-    """(units, iterations per unit, workgroups) of the split a call of op uses."""
+def schedule_info(op: int, N: int, K: int, M: int = 8):
+    """(units, iterations per unit, workgroups) of the split a call of op with
+    M rows uses (M matters only for the NVFP4 ops: M <= 8 or M > 8)."""
     u, i, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    _check(lib().vq_schedule_info(op, N, K, ctypes.byref(u), ctypes.byref(i), ctypes.byref(g)))
+    _check(lib().vq_schedule_info(op, M, N, K, ctypes.byref(u), ctypes.byref(i), ctypes.byref(g)))
     return u.value, i.value, g.value
 
 

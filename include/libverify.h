@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define VQ_ABI_VERSION 7
+#define VQ_ABI_VERSION 8
 
 typedef enum {
   VQ_OK = 0,
@@ -374,16 +374,20 @@ int32_t vq_gdn_commit(const float* state_in, float* state_out, const float* q, c
 size_t vq_workspace_bytes(int32_t op, int32_t M, int32_t N, int32_t K);
 
 /* The split-K / stream-K schedule a call of `op` (not VQ_OP_SAMPLE) uses at
- * (N, K), for inspection and host-side checks ("Beating Splash on an M5
+ * (M, N, K), for inspection and host-side checks ("Beating Splash on an M5
  * Max ...", section "The kernels were not the gap": split-K on the narrow
  * projections). The iteration space is units x iterations, W = units * (K /
  * 128); workgroup g of G owns iterations [g W / G, (g + 1) W / G), unit-major.
  * A unit is a 64-row tile of the packed weights (64 output columns, 32 with
  * SILU_MUL); for VQ_OP_FP8_ACCUMULATE half a tile (32 output columns), and
- * then no unit is shared by more than two workgroups. Writes units,
- * iterations per unit and G; returns VQ_OK, or VQ_ERR_NULL / VQ_ERR_SHAPE /
- * VQ_ERR_VALUE. M does not enter: the schedule depends on (op, N, K) only. */
-int32_t vq_schedule_info(int32_t op, int32_t N, int32_t K, int32_t* units, int32_t* iters, int32_t* workgroups);
+ * then no unit is shared by more than two workgroups; for the NVFP4 ops
+ * (VQ_OP_NVFP4, VQ_OP_NVFP4_SILU_MUL, VQ_OP_LMHEAD) at M > 8 on outputs of
+ * at least 2,048 tiles, a pair of adjacent tiles (the last one alone when the
+ * tile count is odd). M enters only through that choice (M <= 8 or
+ * M > 8). Writes units, iterations per unit and G; returns VQ_OK, or
+ * VQ_ERR_NULL / VQ_ERR_SHAPE / VQ_ERR_VALUE. */
+int32_t vq_schedule_info(int32_t op, int32_t M, int32_t N, int32_t K, int32_t* units, int32_t* iters,
+                         int32_t* workgroups);
 
 const char* vq_status_str(int32_t status);
 const char* vq_last_error(void);

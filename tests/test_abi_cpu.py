@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = ops.lib()
-    assert L.vq_abi_version() == 7
+    assert L.vq_abi_version() == 8
     assert ops.status_str(ops.VQ_OK) == "VQ_OK"
     assert ops.status_str(ops.VQ_ERR_WORKSPACE) == "VQ_ERR_WORKSPACE"
     assert ops.status_str(99) == "VQ_ERR_UNKNOWN"

@@ -102,6 +102,8 @@ def test_nvfp4_single_gemm_m8_k512_n1024():
     (24, 64, 1024, 1.0), (32, 200, 256, 0.125), (8, 4096, 2048, 1.0), (5, 1000, 5120, 1.0),
     (16, 2, 128, 1.0), (8, 65, 128, 1.0), (9, 130, 768, 1.0), (7, 3000, 17408, 1.0),
     (17, 70, 384, 1.0), (29, 130, 640, 0.5),
+    # >= 2,048 tiles at M > 8: tile pairs (an odd tile count, then an even one)
+    (13, 64 * 2049 - 5, 128, 1.0), (32, 64 * 2050, 256, 0.5),
 ])
 def test_nvfp4_shapes(m, n, k, ts):
     say(f"case: NVFP4 M={m} N={n} K={k} ts={ts}")
@@ -155,6 +157,38 @@ def test_nvfp4_silu_mul_small():
     r = run_nvfp4(x, codes, scales, 1.0, inter, epi=1)
     check_f32(r["f32"], h, what="silu*up f32")
     check_bf16_store(r["bf16"], r["f32"], h)
+
+
+def test_nvfp4_silu_mul_tile_pairs():
+    # M > 8 on >= 2,048 tiles: tile pairs, the last one alone (odd count)
+    m, inter, k = 16, 32 * 2049, 128
+    x = inputs.x_bf16((116,), m, k)
+    codes, scales = inputs.nvfp4_weights((116,), 2 * inter, k)
+    h, hb = O.mlp_silu_mul(x, codes, scales, 1.0, inter)
+    r = run_nvfp4(x, codes, scales, 1.0, inter, epi=1)
+    check_f32(r["f32"], h, what="silu*up f32 (tile pairs)")
+    check_bf16_store(r["bf16"], r["f32"], h)
+
+
+def test_tile_pair_rows_independent_of_m():
+    # the scaled family's tile-pair split depends on (N, K) only: rows shared
+    # by calls at M = 9..32 are bitwise equal
+    torch, dev = torch_dev()
+    ops = _ops()
+    n, k = 64 * 2050, 256
+    codes, scales = inputs.nvfp4_weights((117,), n, k)
+    x32 = inputs.x_bf16((117,), 32, k)
+    w = ops.pack_nvfp4(to_dev_u8(codes), to_dev_u8(scales))
+    ws = ops.workspace(ops.VQ_OP_NVFP4, 32, n, k, dev)
+    outs = {}
+    for m in (32, 9, 16, 24):
+        say(f"case: tile pairs M={m}")
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        ops.vq_gemm_nvfp4(to_dev_bf16(x32[:m]), w, 1.0, y, workspace=ws)
+        outs[m] = y.cpu().numpy()
+    for m in (9, 16, 24):
+        assert np.array_equal(outs[m], outs[32][:m]), m
+    check_f32(outs[32], O.gemm_nvfp4(x32, codes, scales, 1.0), what="tile pairs M=32")
 
 
 def test_mlp_layer_m8_full_size():

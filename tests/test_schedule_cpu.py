@@ -82,9 +82,31 @@ def test_the_pass_shapes_get_their_documented_splits():
     }
     for (op, n, k), w in want.items():
         assert ops.schedule_info(op, n, k) == w, (op, n, k)
+        assert ops.schedule_info(op, n, k, M=1) == w, (op, n, k)
+    # M > 8: the NVFP4 ops on outputs of >= 2,048 tiles (the vocabulary head)
+    # stream tile pairs (one activation load feeds 128 columns); narrower
+    # NVFP4 and every FP8 split stay as at M <= 8
+    wide = {(ops.VQ_OP_LMHEAD, 248320, 5120): (1940, 40, 248)}
+    for m in (9, 16, 24, 32):
+        for (op, n, k), w in want.items():
+            assert ops.schedule_info(op, n, k, M=m) == wide.get((op, n, k), w), (op, n, k, m)
+    # an odd tile count: the last pair is one tile
+    assert ops.schedule_info(ops.VQ_OP_NVFP4, 64 * 2049 - 5, 256, M=16)[0] == 1025
+    assert ops.schedule_info(ops.VQ_OP_NVFP4_SILU_MUL, 32 * 2049, 256, M=9)[0] == 1025
+    assert ops.schedule_info(ops.VQ_OP_NVFP4, 64 * 2047, 256, M=16)[0] == 2047  # below 2,048 tiles: tiles
     # the out-projections' units: exactly two shares each
     sh = shares_per_unit(160, 48, 240)
     assert sh.min() == 2 and sh.max() == 2
+
+
+def test_workspace_serves_both_nvfp4_families():
+    # one workspace of (op, N, K) for every M: sized for the larger of the
+    # M <= 8 (tiles) and M > 8 (tile pairs) layouts
+    L = ops.lib()
+    for op, n, k in ((ops.VQ_OP_NVFP4_SILU_MUL, 17408, 5120), (ops.VQ_OP_LMHEAD, 248320, 5120),
+                     (ops.VQ_OP_NVFP4, 64 * 2049 - 5, 256)):
+        sizes = {L.vq_workspace_bytes(op, m, n, k) for m in (1, 8, 9, 32)}
+        assert len(sizes) == 1 and sizes.pop() > 0, (op, n, k)
 
 
 def test_schedule_info_validates():
@@ -92,8 +114,10 @@ def test_schedule_info_validates():
     L = ops.lib()
     x = ctypes.c_int32()
     p = ctypes.byref(x)
-    assert L.vq_schedule_info(ops.VQ_OP_FP8, 64, 128, None, p, p) == ops.VQ_ERR_NULL
-    assert L.vq_schedule_info(ops.VQ_OP_FP8, 0, 128, p, p, p) == ops.VQ_ERR_SHAPE
-    assert L.vq_schedule_info(ops.VQ_OP_FP8, 64, 100, p, p, p) == ops.VQ_ERR_SHAPE
-    assert L.vq_schedule_info(ops.VQ_OP_SAMPLE, 64, 128, p, p, p) == ops.VQ_ERR_VALUE
-    assert L.vq_schedule_info(99, 64, 128, p, p, p) == ops.VQ_ERR_VALUE
+    assert L.vq_schedule_info(ops.VQ_OP_FP8, 8, 64, 128, None, p, p) == ops.VQ_ERR_NULL
+    assert L.vq_schedule_info(ops.VQ_OP_FP8, 8, 0, 128, p, p, p) == ops.VQ_ERR_SHAPE
+    assert L.vq_schedule_info(ops.VQ_OP_FP8, 8, 64, 100, p, p, p) == ops.VQ_ERR_SHAPE
+    assert L.vq_schedule_info(ops.VQ_OP_SAMPLE, 8, 64, 128, p, p, p) == ops.VQ_ERR_VALUE
+    assert L.vq_schedule_info(99, 8, 64, 128, p, p, p) == ops.VQ_ERR_VALUE
+    assert L.vq_schedule_info(ops.VQ_OP_NVFP4, 0, 64, 128, p, p, p) == ops.VQ_ERR_SHAPE
+    assert L.vq_schedule_info(ops.VQ_OP_NVFP4, 33, 64, 128, p, p, p) == ops.VQ_ERR_SHAPE
