@@ -415,26 +415,26 @@ __device__ __forceinline__ void load_w(WBuf<FMT, NT>& b, const uint8_t* blk, con
 // (stage_x). An A operand for one 32-K step is 16 rows x 64 B: loaded
 // directly it would touch half of 16 lines per instruction, twice the line
 // requests per byte.
-//  kLines16 (16-row groups: the scaled NVFP4 family, FP8 and affine at
-//    M > 8): 4 loads per row group and iteration, rows 0-7 and 8-15 of each
+//  A full 16-row group: 4 loads per iteration, rows 0-7 and 8-15 of each
 //    half of the iteration's k range.
-//  kLines8 (M <= 8: the NVFP4 M <= 8 family, and the FP8 and affine kernels
-//    instantiated for at most 8 rows): 2 loads per iteration, rows 0-7. The
-//    NVFP4 A operand holds the rows twice with zeros in between (rows 0-7 on
-//    k-groups 0,1, rows 8-15 on k-groups 2,3; see compute_iter); the 16-row
-//    kernels' rows 8-15 are padding. Lanes that hold zeros read a zeroed slot.
+//  A half group (LAST8: the last group holds at most 8 rows -- M <= 8 for the
+//    16-row kernels, M = 17-24 for two groups -- and the NVFP4 M <= 8
+//    family): 2 loads, rows 0-7. The NVFP4 A operand holds the rows twice
+//    with zeros in between (rows 0-7 on k-groups 0,1, rows 8-15 on k-groups
+//    2,3; see compute_iter); the 16-row kernels' rows 8-15 of a half group
+//    are padding. Lanes that hold zeros read a zeroed slot.
 // Lane l reads row l >> 3 (+ 8 for the second half of a 16-row group),
 // 16-byte segment (l & 7) ^ (l >> 3) of the line, and its 16 bytes land at
 // position l & 7 of that row in LDS: the swizzle keeps the fragment reads
 // free of bank conflicts.
-enum XMode { kLines16 = 1, kLines8 = 2 };
-
-template <int FMT, int RG, bool R8 = false>
+template <int FMT, int RG, bool LAST8 = false>
 struct XCursor {
-  static constexpr int kMode = (FMT == FMT_NVFP4 || R8) ? kLines8 : kLines16;
-  static_assert(kMode != kLines8 || RG == 1, "at most 8 rows: one row group");
+  // the last row group is a half group
+  static constexpr bool kHalf = FMT == FMT_NVFP4 || LAST8;
+  static_assert(FMT != FMT_NVFP4 || RG == 1, "the NVFP4 M <= 8 family has one row group");
+  static constexpr bool half_group(int rg) { return kHalf && rg == RG - 1; }
   const uint16_t* row[RG];   // rows 0-7 of each row group
-  const uint16_t* half[RG];  // kLines16: rows 8-15
+  const uint16_t* half[RG];  // full groups: rows 8-15
   __device__ __forceinline__ void init(const GemmParams& p, int lane) {
     const int r = lane >> 3, seg = (lane & 7) ^ r;
 #pragma unroll
@@ -446,17 +446,16 @@ struct XCursor {
       half[rg] = p.x + (size_t)m1 * p.K + 8 * seg;
     }
   }
-  // kLines16: b.xa[rg][c] holds rows 8 (c & 1) .. +7 of k 64 (c >> 1) .. +63.
-  // kLines8: b.xa[0][c], c = 0, 1, holds rows 0-7 of k 64 c .. +63.
+  // Full group: b.xa[rg][c] holds rows 8 (c & 1) .. +7 of k 64 (c >> 1) ..
+  // +63. Half group: b.xa[rg][c], c = 0, 1, holds rows 0-7 of k 64 c .. +63.
   __device__ __forceinline__ void load(XBuf<RG>& b, int kit) const {
-    if constexpr (kMode == kLines8) {
-      const uint16_t* lo = row[0] + (size_t)(kit * kIterK);
-      b.xa[0][0] = ld16(lo);
-      b.xa[0][1] = ld16(lo + 64);
-    } else {
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-        const uint16_t* lo = row[rg] + (size_t)(kit * kIterK);
+    for (int rg = 0; rg < RG; ++rg) {
+      const uint16_t* lo = row[rg] + (size_t)(kit * kIterK);
+      if (half_group(rg)) {
+        b.xa[rg][0] = ld16(lo);
+        b.xa[rg][1] = ld16(lo + 64);
+      } else {
         const uint16_t* hi = half[rg] + (size_t)(kit * kIterK);
         b.xa[rg][0] = ld16(lo);
         b.xa[rg][1] = ld16(hi);
@@ -469,46 +468,54 @@ struct XCursor {
 
 // Activation staging: one chunk per (row group, load) holds 8 rows x 128 B;
 // 1152 B per chunk rather than 1024 puts the two row halves of a fragment
-// read on different banks. kLines8 adds one zeroed 16-byte slot after its two
-// chunks.
+// read on different banks. Full groups come first (4 chunks each), then a
+// half group's 2 chunks and one zeroed 16-byte slot.
 constexpr int kXChunk = 72;  // u32x4 per chunk
-template <int MODE, int RG>
+template <int RG, bool HALF>
 struct XStage {
-  static constexpr int kZero = 2 * kXChunk;  // kLines8: the zero slot
-  static constexpr int kSize = MODE == kLines8 ? 2 * kXChunk + 8 : 4 * RG * kXChunk;
+  static constexpr int kChunks = HALF ? 4 * (RG - 1) + 2 : 4 * RG;
+  static constexpr int kZero = kChunks * kXChunk;  // HALF: the zero slot
+  static constexpr int kSize = kChunks * kXChunk + (HALF ? 8 : 0);
 };
 
 // Whole-line registers (see XCursor::load) -> MFMA A operands, through this
 // wave's LDS area xs. The wave barriers keep the compiler from moving the LDS
 // reads above the writes, or the next call's writes above this call's reads;
 // a wave's LDS operations execute in order.
-template <int MODE, int RG, int FMT>
+template <typename XC, int RG, int FMT>
 __device__ __forceinline__ void stage_x(const XBuf<RG>& in, XBuf<RG>& out, u32x4_t* xs, int lane) {
+  using XS = XStage<RG, XC::kHalf>;
   __builtin_amdgcn_wave_barrier();
-  constexpr int NC = MODE == kLines8 ? 2 : 4;
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
+  for (int rg = 0; rg < RG; ++rg) {
+    if (XC::half_group(rg)) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) xs[(rg * NC + c) * kXChunk + lane] = in.xa[rg][c];
+      for (int c = 0; c < 2; ++c) xs[(4 * rg + c) * kXChunk + lane] = in.xa[rg][c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xs[(4 * rg + c) * kXChunk + lane] = in.xa[rg][c];
+    }
+  }
   __builtin_amdgcn_wave_barrier();
   const int i = lane & 15, g = lane >> 4;  // MFMA A operand: row i, k 8 g .. +7 of the step
-  if constexpr (MODE == kLines8) {
-    const bool carries = FMT == FMT_NVFP4 ? (i >> 3) == (g >> 1) : i < 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int seg = 4 * (j & 1) + g;
-      const int at = carries ? (j >> 1) * kXChunk + (i & 7) * 8 + (seg ^ (i & 7)) : XStage<MODE, RG>::kZero;
-      out.xa[0][j] = xs[at];
-    }
-  } else {
+  for (int rg = 0; rg < RG; ++rg) {
+    if (XC::half_group(rg)) {
+      const bool carries = FMT == FMT_NVFP4 ? (i >> 3) == (g >> 1) : i < 8;
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
+      for (int j = 0; j < 4; ++j) {
+        const int seg = 4 * (j & 1) + g;
+        const int at = carries ? (4 * rg + (j >> 1)) * kXChunk + (i & 7) * 8 + (seg ^ (i & 7)) : XS::kZero;
+        out.xa[rg][j] = xs[at];
+      }
+    } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = 2 * (j >> 1) + (i >> 3);
         const int seg = 4 * (j & 1) + g;
-        out.xa[rg][j] = xs[(rg * 4 + c) * kXChunk + (i & 7) * 8 + (seg ^ (i & 7))];
+        out.xa[rg][j] = xs[(4 * rg + c) * kXChunk + (i & 7) * 8 + (seg ^ (i & 7))];
       }
+    }
   }
   __builtin_amdgcn_wave_barrier();
 }
@@ -916,15 +923,17 @@ struct Occupancy {
 // first loads are issued without waiting on a kernel-argument fetch
 // (measured 1 % over the pass). The rest of the parameters follow in p.
 //
-// RGX: the row groups, or 0 for a 16-row kernel (FP8, affine) launched with
-// M <= 8: one row group whose rows 8-15 are padding, so its activation loads
-// read only rows 0-7. NT: sub-tiles per unit of the schedule (2: half tiles of
-// the accumulating epilogue; 4: tiles; 8: tile pairs, scaled NVFP4 only).
+// RGX: the row groups (1, 2), or a count whose last 16-row group holds at
+// most 8 rows, so its activation loads read only those: 0 = one such group
+// (FP8 and affine at M <= 8), 3 = two groups, the second of them such a
+// group (16-row kernels at M = 17-24). NT: sub-tiles per unit of the schedule
+// (2: half tiles of the accumulating epilogue; 4: tiles; 8: tile pairs,
+// scaled NVFP4 only).
 template <int FMT, int EPI, int RGX, int NT>
 __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_kernel(
     const uint8_t* a_w, const uint16_t* a_x, int64_t a_total, int32_t a_wgs,
     int32_t a_iters, int32_t a_K, int32_t a_M, GemmParams p) {
-  constexpr int RG = RGX == 0 ? 1 : RGX;
+  constexpr int RG = RGX == 0 ? 1 : RGX == 3 ? 2 : RGX;
   p.w = a_w;
   p.x = a_x;
   p.total = a_total;
@@ -941,9 +950,9 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_ker
   constexpr int SLOT = NT * REGS * 64;
   constexpr size_t BLOCK = FMT == FMT_FP8 ? kBlockF8 : kBlockF4;
   __shared__ float lds[4 * SLOT];
-  using XC = XCursor<FMT, RG, RGX == 0>;
-  constexpr int XMODE = XC::kMode;
-  constexpr int XS = XStage<XMODE, RG>::kSize;  // activation staging per wave
+  using XC = XCursor<FMT, RG, RGX == 0 || RGX == 3>;
+  using XST = XStage<RG, XC::kHalf>;
+  constexpr int XS = XST::kSize;  // activation staging per wave
   __shared__ u32x4_t xstage[4 * XS];
 
   const int lane = threadIdx.x & 63;
@@ -981,7 +990,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_ker
     const uint8_t* wnext = unit_base(lu) + (size_t)(s - lu * I) * BLOCK;
     XC xc;
     xc.init(p, lane);
-    if constexpr (XMODE == kLines8) xstage[q * XS + XStage<XMODE, RG>::kZero] = u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (XC::kHalf) xstage[q * XS + XST::kZero] = u32x4_t{0u, 0u, 0u, 0u};
     int xkit = (int)(s - (int64_t)first_tile * I);
     int64_t lit = s;  // next iteration to load
 
@@ -1015,7 +1024,7 @@ __global__ __launch_bounds__(256, (Occupancy<FMT, RGX>::value)) void vq_gemm_ker
 
     auto compute = [&](int qq) {
       XBuf<RG> xt;
-      stage_x<XMODE, RG, FMT>(xb[qq], xt, xstage + q * XS, lane);
+      stage_x<XC, RG, FMT>(xb[qq], xt, xstage + q * XS, lane);
       compute_iter<FMT, RG, NT>(wb[qq], xt, acc);
     };
 
@@ -1208,18 +1217,25 @@ static int launch_rg(const GemmParams& p, hipStream_t st) {
     (void)rg;  // launch_gemm sends M > 8 to the scaled family
     hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
                        p.iters, p.K, p.M, p);
-  } else if constexpr (FMT == FMT_NVFP4S) {
-    if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
-                       p.iters, p.K, p.M, p);
-    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
-                       p.iters, p.K, p.M, p);
   } else {
-    if (p.M <= 8) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 0, NT>), grid, block, 0, st, p.w, p.x, p.total,
-                       p.wgs, p.iters, p.K, p.M, p);
-    else if (rg == 1) hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
-                       p.iters, p.K, p.M, p);
-    else hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
-                       p.iters, p.K, p.M, p);
+    // 16-row groups; a last group of at most 8 rows gets the instance that
+    // reads only those (M <= 8 for FP8 and affine; M = 17-24)
+    if constexpr (FMT != FMT_NVFP4S) {
+      if (p.M <= 8) {
+        hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 0, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
+                           p.iters, p.K, p.M, p);
+        return (int)hipGetLastError();
+      }
+    }
+    if (rg == 1)
+      hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 1, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
+                         p.iters, p.K, p.M, p);
+    else if (p.M <= 24)
+      hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 3, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
+                         p.iters, p.K, p.M, p);
+    else
+      hipLaunchKernelGGL((vq_gemm_kernel<FMT, EPI, 2, NT>), grid, block, 0, st, p.w, p.x, p.total, p.wgs,
+                         p.iters, p.K, p.M, p);
   }
   return (int)hipGetLastError();
 }
