@@ -73,7 +73,7 @@ def check_head(out, logits_ref, drafts, lanes, R):
     (1, 8, 5000, 512, 1.0), (4, 8, 3001, 256, 0.5), (2, 5, 777, 1024, 1.0), (3, 1, 100, 128, 1.0),
     (1, 2, 64, 128, 2.0), (4, 3, 20000, 384, 1.0), (2, 4, 1111, 640, 1.0),
     # >= 2,048 tiles at M > 8: tile pairs, the second with an odd tile count
-    (2, 8, 64 * 2050, 128, 1.0), (4, 8, 64 * 2049 - 11, 256, 0.5),
+    (2, 8, 64 * 2050, 128, 1.0), (4, 8, 64 * 2049 - 11, 256, 0.5), (3, 8, 64 * 2049 - 11, 128, 1.0),
 ])
 def test_head_random(lanes, R, V, K, ts):
     say(f"case: head lanes={lanes} R={R} V={V} K={K}")

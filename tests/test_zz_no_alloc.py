@@ -75,6 +75,16 @@ def test_noalloc_matches_workspace_entry_point_across_shapes():
                        s3.cpu().numpy()[rows], 1.0)
     check_f32(a3.cpu().numpy()[:, rows], ref, what="no-alloc down M=16 (sampled columns)")
 
+    # 3b. tile pairs (the scaled family on >= 2,048 tiles, an odd count) at M = 24
+    say("case: no-alloc tile pairs N=131131 K=256 at M=24, fp32")
+    n5, k5 = 64 * 2049 - 5, 256
+    x5 = inputs.x_bf16((500, 5), 24, k5)
+    c5, s5 = inputs.nvfp4_weights((500, 5), n5, k5)
+    w5 = ops.pack_nvfp4(to_dev_u8(c5), to_dev_u8(s5))
+    a5, b5 = _pair(to_dev_bf16(x5), w5, 1.0, n5, 24, ops.VQ_EPI_NONE, f32)
+    assert _same(a5, b5)
+    check_f32(a5.cpu().numpy(), O.gemm_nvfp4(x5, c5, s5, 1.0), what="no-alloc tile pairs M=24")
+
     # 4. the first shape again: the counters the smaller calls used were left at zero
     say("case: no-alloc [gate;up] again after the other shapes")
     a4, _ = _pair(x1, w1, 1.0, inter, 8, ops.VQ_EPI_SILU_MUL, bf)
