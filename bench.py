@@ -217,6 +217,22 @@ def replay_ms(torch, g, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def replay_stats(torch, g, reps=50):
+    """ms of `reps` single replays, each between HIP events on the stream the
+    graph is launched on and followed by a synchronize (median, min, max)."""
+    import numpy as np
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return {"replays": reps, "median": round(float(np.median(ts)), 4), "min": round(float(np.min(ts)), 4),
+            "max": round(float(np.max(ts)), 4)}
+
+
 def per_kind_durations(torch, p, reps=3):
     """Average duration of each launch kind of the pass: every launch of that
     kind (rotating over the layers' weights, so nothing is cached) captured in
@@ -875,6 +891,10 @@ def main():
     gbps = p.weight_bytes / dt / 1e9
     log(f"pass: {dt * 1e3:.3f} ms, {gbps:.0f} GB/s effective")
 
+    # single replays (outside the timed region): spread of the pass time
+    replays = replay_stats(torch, g)
+    log(f"single replays: {replays}")
+
     # eager (ungraphed) pass: what the graph saves
     t0 = time.perf_counter()
     p.run()
@@ -939,6 +959,8 @@ def main():
         "measured_read_gbps": round(probes["read"], 1),
         "target_80pct_of_measured_bw": target,
         "tok_s_at_alpha_4_80": round(ALPHA / dt, 1),
+        "pass_replay_ms": replays,
+        "sum_of_kernel_times_ms": round(sum(v["avg_us"] * v["launches_per_pass"] for v in kinds.values()) / 1e3, 4),
         "eager_ms_per_pass": round(eager_ms, 3),
         "accept_len_last_pass": accept,
         "kernels": kinds,
