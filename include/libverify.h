@@ -60,7 +60,9 @@
  *     counters, argmax buckets, done counter) is placed from those three
  *     values, and a call with another op, N or K would find its counters on
  *     the previous shape's non-zero partial sums. Within that binding it
- *     serves every M (the size and layout do not depend on M). Kernels leave
+ *     serves every M (the size does not depend on M; the NVFP4 ops at M > 8
+ *     may use a schedule of tile pairs, laid out in the same size, and every
+ *     call leaves the counters zeroed). Kernels leave
  *     every counter in it at zero again, so a bound workspace can be reused
  *     by any number of stream-ordered calls (and graph replays); reusing it
  *     for another (op, N, K) requires zero-filling it again first. Two calls
@@ -68,9 +70,9 @@
  *     workspace returns VQ_ERR_WORKSPACE; the schedule never changes
  *     silently.
  *   - Results are deterministic: the K partition and the order of the fixed
- *     split-K reduction depend only on (N, K) and the epilogue, never on M.
- *     FP8 and affine 4-bit: row r of an M-row call equals row r of any other
- *     M bit for bit.
+ *     split-K reduction depend only on (N, K) and the epilogue, and for NVFP4
+ *     on the family below, never on M otherwise. FP8 and affine 4-bit: row r
+ *     of an M-row call equals row r of any other M bit for bit.
  *     NVFP4 has two compute families with different rounding (M <= 8: the
  *     block scale multiplies each block's fp32 partial sum; M > 8: the weights
  *     are scaled before the MFMA, exactly, and summed in fp32), and rows agree
