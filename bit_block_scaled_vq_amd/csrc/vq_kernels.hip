@@ -890,14 +890,16 @@ __device__ __forceinline__ void reduce_tile(const GemmParams& p, int tile, int l
 // activation ring would cap the weight prefetch at its depth).
 template <int FMT, int RG, int NT = kNT>
 struct PipeDepth {
-  // wide row groups: the activation ring would spill; scaled NVFP4 with two
-  // row groups keeps 2 (3 and 4 measured slower at M = 24 and 32). One row
-  // group: 3 (4 measured slower for NVFP4 M <= 8 and FP8 M <= 8).
-  // Half-tile units carry half the weight bytes per iteration: 5 deep at one
-  // row group (4 and 6 measured slower on 5,120 x 6,144 at M = 8). Tile pairs
-  // keep the tiles' depths (twice the weight bytes per slot).
-  static constexpr int value = NT < kNT ? (RG == 1 ? 5 : 3)
-                                        : (FMT == FMT_NVFP4S && RG == 2) ? 2 : (RG <= 2 ? 3 : 2);
+  // Measured with the whole-line activation loads (interleaved pass replays;
+  // deeper rings and refilling a slot before its compute were slower, so more
+  // bytes in flight per wave do not help): NVFP4, both families, 2 (3 and 4
+  // slower; 2 took the M = 8 pass 4.18 -> 4.14 ms and the 2-lane pass
+  // 4.69 -> 4.55 ms); FP8 3 at one row group (2 and 4 slower), 2 at two;
+  // half-tile units 3 at one row group (2, 4 and 5 slower), 2 at two; affine
+  // 3.
+  static constexpr int value = NT < kNT ? (RG == 1 ? 3 : 2)
+                               : (FMT == FMT_NVFP4 || FMT == FMT_NVFP4S) ? 2
+                               : (FMT == FMT_FP8 && RG == 2) ? 2 : 3;
 };
 // Workgroups per CU the register budget is sized for. Every launch has at
 // most one workgroup per CU (at most 256 workgroups of 4 waves), so one wave
