@@ -373,10 +373,23 @@ struct XBuf {
 
 // Weights are read once per pass: non-temporal loads stream them without
 // displacing the activations, partial sums and counters from L2 and the MALL
-// (measured 5 % faster over the whole pass than ordinary loads).
-__device__ __forceinline__ u32x4_t ldnt(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
+// (measured 5 % faster over the whole pass than ordinary loads). They are
+// buffer loads off a resource per block: the block's address sits in SGPRs
+// and each lane supplies a 32-bit offset, so the ring's loads cost no 64-bit
+// address arithmetic (M = 8 pass 0.3-0.5 % faster than global loads on three
+// boxes; adding the scope bits to the non-temporal hint changed nothing).
+// The resource's range is the bytes the unit reads from that base, so an
+// offset past it reads zeros instead of another block.
+constexpr int kBufNT = 2;           // cache-policy operand: non-temporal
+constexpr int kBufWord3 = 0x00020000;  // resource word 3 for raw dword access
+struct WRes {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ WRes(const uint8_t* base, int bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, kBufWord3)) {}
+  __device__ __forceinline__ u32x4_t ld(int off) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufNT);
+  }
+};
 
 // blk: the block, or for a half-tile unit (NT = 2, FP8 only) the start of the
 // half's two sub-tiles inside its block; blk2: a tile pair's second block.
@@ -385,26 +398,30 @@ __device__ __forceinline__ void load_w(WBuf<FMT, NT>& b, const uint8_t* blk, con
   static_assert(NT == kNT || (NT < kNT && FMT == FMT_FP8) || (NT > kNT && FMT == FMT_NVFP4S),
                 "half-tile units are FP8 only, tile pairs scaled NVFP4 only");
   if constexpr (NT > kNT) {
+    const WRes w(blk, kBlockF4), w2(blk2, kBlockF4);
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) b.c[t] = ldnt(blk + t * 1024 + lane * 16);
+    for (int t = 0; t < kNT; ++t) b.c[t] = w.ld(t * 1024 + lane * 16);
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) b.c[kNT + t] = ldnt(blk2 + t * 1024 + lane * 16);
-    b.s[0] = ldnt(blk + 4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
-    b.s[1] = ldnt(blk2 + 4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
+    for (int t = 0; t < kNT; ++t) b.c[kNT + t] = w2.ld(t * 1024 + lane * 16);
+    b.s[0] = w.ld(4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
+    b.s[1] = w2.ld(4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
   } else if constexpr (FMT == FMT_AFFINE) {
+    const WRes w(blk, kBlockF4);
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) b.c[t] = ldnt(blk + t * 1024 + lane * 16);
-    b.sb[0] = ldnt(blk + 4096 + (lane & 15) * 32);
-    b.sb[1] = ldnt(blk + 4096 + (lane & 15) * 32 + 16);
+    for (int t = 0; t < kNT; ++t) b.c[t] = w.ld(t * 1024 + lane * 16);
+    b.sb[0] = w.ld(4096 + (lane & 15) * 32);
+    b.sb[1] = w.ld(4096 + (lane & 15) * 32 + 16);
   } else if constexpr (FMT != FMT_FP8) {
+    const WRes w(blk, kBlockF4);
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) b.c[t] = ldnt(blk + t * 1024 + lane * 16);
-    b.s = ldnt(blk + 4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
+    for (int t = 0; t < kNT; ++t) b.c[t] = w.ld(t * 1024 + lane * 16);
+    b.s = w.ld(4096 + (((lane >> 5) * 16) + (lane & 15)) * 16);
   } else {
+    const WRes w(blk, NT * 2048);  // a half-tile unit reads half of its block
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      b.c[t][0] = ldnt(blk + (t * 2 + 0) * 1024 + lane * 16);
-      b.c[t][1] = ldnt(blk + (t * 2 + 1) * 1024 + lane * 16);
+      b.c[t][0] = w.ld((t * 2 + 0) * 1024 + lane * 16);
+      b.c[t][1] = w.ld((t * 2 + 1) * 1024 + lane * 16);
     }
   }
 }
