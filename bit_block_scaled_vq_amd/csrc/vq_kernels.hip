@@ -139,11 +139,16 @@ __device__ __forceinline__ bf16x8_t dec_fp8x8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
-__device__ __forceinline__ float scale_byte(uint32_t w, int j) {
-  if (j == 0) return __builtin_amdgcn_cvt_f32_fp8(w, 0);
-  if (j == 1) return __builtin_amdgcn_cvt_f32_fp8(w, 1);
-  if (j == 2) return __builtin_amdgcn_cvt_f32_fp8(w, 2);
-  return __builtin_amdgcn_cvt_f32_fp8(w, 3);
+// The four E4M3 block scales of one dword (byte j = block j) as fp32, two per
+// convert: 8 instead of 16 scale converts per iteration, the same values
+// (M = 16 [gate; up] 26.4 -> 25.0 us, the 4-lane pass 5.94 -> 5.86 ms).
+__device__ __forceinline__ void scales4(uint32_t w, float (&s)[4]) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  s[0] = lo[0];
+  s[1] = lo[1];
+  s[2] = hi[0];
+  s[3] = hi[1];
 }
 
 // fp32 -> bf16 bits, round to nearest even; NaN -> quiet NaN.
@@ -574,19 +579,24 @@ __device__ __forceinline__ void compute_iter(const WBuf<FMT, NT>& b, const XBuf<
         d[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.xa[0][j]),
                                                           dec_fp4x8(b.c[t][j]), f32x4_t{}, 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t) {
+      float s4[4];
+      scales4(b.scales(t), s4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float sc = scale_byte(b.scales(t), j);
+        const float sc = s4[j];
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc.v[t][r] = __builtin_fmaf(sc, d[t][j][r], acc.v[t][r]);
       }
+    }
   } else if constexpr (FMT == FMT_NVFP4S) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+      float s4[4];
+      scales4(b.scales(t), s4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8_t wv = dec_fp4x8_scaled(b.c[t][j], scale_byte(b.scales(t), j));
+        const bf16x8_t wv = dec_fp4x8_scaled(b.c[t][j], s4[j]);
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
           f32x4_t a = {acc.v[t][4 * rg], acc.v[t][4 * rg + 1], acc.v[t][4 * rg + 2], acc.v[t][4 * rg + 3]};
