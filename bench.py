@@ -753,13 +753,15 @@ def cpu_baseline(inputs_mod):
 
 
 def kernel_source_digest():
-    """sha256 of the kernel sources: stored HBM-traffic figures apply only to
-    the kernels they were counted on."""
+    """sha256 of the kernel sources and the code generation flags: stored
+    HBM-traffic figures apply only to the kernels they were counted on."""
     import hashlib
+    from bit_block_scaled_vq_amd.build import CODEGEN_FLAGS
     h = hashlib.sha256()
     for f in ("vq_kernels.hip", "vq_internal.h", "vq_keys.h"):
         with open(os.path.join(ROOT, "bit_block_scaled_vq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(CODEGEN_FLAGS).encode())
     return h.hexdigest()
 
 
